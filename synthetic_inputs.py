@@ -1,0 +1,150 @@
+"""Seeded synthetic inputs for the patch-layer workloads.
+
+This module only draws random numbers and slices them; it holds none of the
+method's arithmetic, so the oracle side and the HIP side can both take their
+inputs from it.
+
+Workloads are SDXL UNet feature maps at the shapes of the 1024^2, 2048^2 and
+3840^2 latents (SDXL compresses images 8x into its latent space: "阅读论文1_d-
+CSDN博客", section 实验设置, 模型), split by rows into n patches.  The real
+benchmark uses SDXL weights and COCO captions, neither of which is used here:
+seeded N(0,1) activations stand in for them.
+
+Recipe (per workload, torch generator seeded with ``seed``), drawn in this
+order on the chosen device:
+  1. X_full  [B, H, W, C]          ~ N(0, 1)
+  2. noise_x [B, H, W, C]          ~ N(0, 1)
+  3. Q_full, K_full, V_full  [B, H*W, heads, d]  ~ N(0, 1)
+  4. noise_k, noise_v        [B, H*W, heads, d]  ~ N(0, 1)
+  5. conv weight [C, 3, 3, C]      ~ N(0, 1 / (9 C))
+  6. gamma = 1 + 0.1 N(0,1), beta = 0.1 N(0,1)   [C], fp32
+  7. conv bias [C] = 0, or 0.1 N(0,1) with ``nonzero_bias``
+stale maps = full + sigma * noise (or exactly full with ``stale_equals_fresh``);
+fresh tensors are the rows / tokens of patch i of the full maps.  Values are
+rounded (round-to-nearest-even) to the workload dtype after the stale sum.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    batch: int
+    channels: int
+    height: int
+    width: int
+    n_patches: int
+    heads: int
+    head_dim: int = 64
+    groups: int = 32
+    eps: float = 1e-5
+    dtype: str = "bf16"
+    sigma: float = 0.1
+    seed: int = 1000
+    patch: int = 0
+
+    @property
+    def geom(self):
+        return (self.batch, self.height, self.width, self.n_patches, self.patch)
+
+    @property
+    def h(self):
+        return self.height // self.n_patches
+
+    @property
+    def lq(self):
+        return self.h * self.width
+
+    @property
+    def tokens(self):
+        return self.height * self.width
+
+    @property
+    def torch_dtype(self):
+        return torch.float32 if self.dtype == "f32" else torch.bfloat16
+
+    def with_patch(self, i):
+        return replace(self, patch=i)
+
+    # algorithmic work, counted as in the measurement section of the design
+    def attn_flops(self):
+        return 4.0 * self.batch * self.heads * self.lq * self.tokens * self.head_dim
+
+    def conv_flops(self):
+        return 2.0 * self.batch * self.lq * self.channels * self.channels * 9
+
+    def elem_bytes(self):
+        return 4 if self.dtype == "f32" else 2
+
+    def slice_bytes(self):
+        """Bytes of one fresh slice [B, h, W, C]."""
+        return self.batch * self.lq * self.channels * self.elem_bytes()
+
+
+WORKLOADS = {
+    "tiny": Workload("tiny", 1, 128, 32, 32, 2, 2, dtype="f32", sigma=0.05, seed=1001),
+    "sdxl1024_l2": Workload("sdxl1024_l2", 2, 640, 64, 64, 8, 10, seed=1002),
+    "sdxl1024_l3": Workload("sdxl1024_l3", 2, 1280, 32, 32, 4, 20, seed=1003),
+    "sdxl2048_l2": Workload("sdxl2048_l2", 2, 640, 128, 128, 8, 10, seed=1004),
+    "sdxl3840_l2": Workload("sdxl3840_l2", 2, 640, 240, 240, 8, 10, seed=1005),
+    "sdxl3840_l3": Workload("sdxl3840_l3", 2, 1280, 120, 120, 8, 20, seed=1006),
+}
+
+
+def make_inputs(wl: Workload, device="cpu", stale_equals_fresh=False, nonzero_bias=False):
+    """Draw the seeded tensors of ``wl`` and cut out patch ``wl.patch``.
+
+    Returns a dict of contiguous tensors on ``device`` in the workload dtype
+    (gamma, beta, bias in fp32)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed)
+    B, H, W, C = wl.batch, wl.height, wl.width, wl.channels
+    L, nh, d = wl.tokens, wl.heads, wl.head_dim
+    h, i, Lq = wl.h, wl.patch, wl.lq
+    dt = wl.torch_dtype
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+
+    x_full = randn(B, H, W, C)
+    noise_x = randn(B, H, W, C)
+    q_full = randn(B, L, nh, d)
+    k_full = randn(B, L, nh, d)
+    v_full = randn(B, L, nh, d)
+    noise_k = randn(B, L, nh, d)
+    noise_v = randn(B, L, nh, d)
+    weight = randn(C, 3, 3, C) * (1.0 / (9.0 * C)) ** 0.5
+    gamma = 1.0 + 0.1 * randn(C)
+    beta = 0.1 * randn(C)
+    bias = 0.1 * randn(C) if nonzero_bias else torch.zeros(C, device=device)
+
+    s = 0.0 if stale_equals_fresh else wl.sigma
+    x_stale = (x_full + s * noise_x).to(dt)
+    k_stale = (k_full + s * noise_k).to(dt)
+    v_stale = (v_full + s * noise_v).to(dt)
+    del noise_x, noise_k, noise_v
+    out = {
+        "x_fresh": x_full[:, i * h:(i + 1) * h].to(dt).contiguous(),
+        "x_stale": x_stale.contiguous(),
+        "q": q_full[:, i * Lq:(i + 1) * Lq].to(dt).contiguous(),
+        "k_fresh": k_full[:, i * Lq:(i + 1) * Lq].to(dt).contiguous(),
+        "v_fresh": v_full[:, i * Lq:(i + 1) * Lq].to(dt).contiguous(),
+        "k_stale": k_stale.contiguous(),
+        "v_stale": v_stale.contiguous(),
+        "weight": weight.to(dt).contiguous(),
+        "bias": bias.contiguous(),
+        "gamma": gamma.contiguous(),
+        "beta": beta.contiguous(),
+    }
+    return out
+
+
+def make_map(shape, seed, dtype=torch.float32, device="cpu", scale=1.0):
+    """A single seeded N(0, scale^2) tensor, rounded to ``dtype``."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return (scale * torch.randn(*shape, generator=g, device=device, dtype=torch.float32)).to(dtype)
