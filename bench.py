@@ -1,0 +1,292 @@
+"""Benchmark of one device's share of a DistriFusion patch layer on MI355X.
+
+A step is one pass of the whole hot path for the 3840^2 SDXL workload split
+into n = 8 row patches (this device holds patch 4, an interior patch with both
+halos), for both of its UNet feature-map levels:
+  (a) 2 x 640 ch x 240 x 240  (57600 tokens, 10 heads x 64, 7200 local queries)
+  (b) 2 x 1280 ch x 120 x 120 (14400 tokens, 20 heads x 64, 1800 local queries)
+Per level: corrected async GroupNorm -> 3x3 conv with stale halo (its input
+is the GroupNorm output) -> self-attention over fresh + stale K/V -> refresh
+of K, V, the conv input and the GroupNorm moments into the stale buffers.
+Inputs are seeded synthetic bf16 tensors already resident in HBM.
+
+Prints one JSON line.  `value` is (attention + conv FLOPs of both levels) /
+step time in TFLOP/s.  Per-op figures (attention and conv TFLOP/s, GroupNorm
+and refresh GB/s with buffers rotated through > 512 MB so the 256 MB
+Infinity Cache cannot serve them) ride along, plus the roofline of the
+dominant kernel (attention at level a) and the CPU oracle's rate on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+METRIC = "patch-layer TFLOP/s (attn+conv), GroupNorm GB/s, ms/layer at 3840² n=8"
+LEVELS = ("sdxl3840_l2", "sdxl3840_l3")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--patch", type=int, default=4)
+    ap.add_argument("--op-iters", type=int, default=20)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time budget of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+class Level:
+    """Device buffers of one workload level (patch `patch`)."""
+
+    def __init__(self, name, patch, dev):
+        import torch
+
+        import displaced_patch_parallelism_distri_amd as dp
+        import synthetic_inputs as si
+
+        self.wl = wl = si.WORKLOADS[name].with_patch(patch)
+        self.geom = wl.geom
+        d = si.make_inputs(wl, device=dev, nonzero_bias=True)
+        self.t = d
+        B, n, G, C = wl.batch, wl.n_patches, wl.groups, wl.channels
+        # the previous step's per-patch GroupNorm moments: run the op on every
+        # stale patch and refresh each result into the table
+        self.table = torch.zeros(B, n, G, 2, dtype=torch.float32, device=dev)
+        scratch_table = torch.zeros_like(self.table)
+        for j in range(n):
+            gj = (B, wl.height, wl.width, n, j)
+            xs_j = d["x_stale"][:, j * wl.h:(j + 1) * wl.h].contiguous()
+            _, fm = dp.distri_async_groupnorm(gj, G, xs_j, scratch_table, d["gamma"], d["beta"])
+            dp.distri_refresh_stale((B, n, 1, n, j), 2 * G, fm, self.table)
+        self.conv_stale = d["x_stale"]          # stale conv input map (GN output of last step)
+        self.y_gn = torch.empty_like(d["x_fresh"])
+        self.fm = torch.empty(B, G, 2, dtype=torch.float32, device=dev)
+        self.y_conv = torch.empty(B, wl.h, wl.width, C, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty_like(d["q"])
+        self.gn_ws = torch.empty(dp.distri_async_groupnorm_workspace_size(self.geom, C, G, dp.DISTRI_BF16),
+                                 dtype=torch.uint8, device=dev)
+        nb = dp.distri_patch_self_attn_workspace_size(self.geom, wl.heads, 64, dp.DISTRI_BF16)
+        self.attn_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
+        self.tok_row = wl.width * wl.heads * wl.head_dim
+        self.scale = wl.head_dim ** -0.5
+
+    # the individual ops -------------------------------------------------
+    def groupnorm(self, x=None, y=None):
+        import displaced_patch_parallelism_distri_amd as dp
+
+        dp.distri_async_groupnorm(self.geom, self.wl.groups, self.t["x_fresh"] if x is None else x,
+                                  self.table, self.t["gamma"], self.t["beta"], eps=self.wl.eps,
+                                  y=self.y_gn if y is None else y, fresh_moments=self.fm,
+                                  workspace=self.gn_ws)
+
+    def conv(self):
+        import displaced_patch_parallelism_distri_amd as dp
+
+        dp.distri_patch_conv3x3_halo(self.geom, self.y_gn, self.conv_stale, self.t["weight"],
+                                     self.t["bias"], y=self.y_conv)
+
+    def attention(self):
+        import displaced_patch_parallelism_distri_amd as dp
+
+        t = self.t
+        dp.distri_patch_self_attn(self.geom, self.wl.heads, t["q"], t["k_fresh"], t["v_fresh"],
+                                  t["k_stale"], t["v_stale"], out=self.out, scale=self.scale,
+                                  workspace=self.attn_ws)
+
+    def refresh(self):
+        import displaced_patch_parallelism_distri_amd as dp
+
+        t, wl = self.t, self.wl
+        dp.distri_refresh_stale(self.geom, self.tok_row, t["k_fresh"], t["k_stale"])
+        dp.distri_refresh_stale(self.geom, self.tok_row, t["v_fresh"], t["v_stale"])
+        dp.distri_refresh_stale(self.geom, wl.width * wl.channels, self.y_gn, self.conv_stale)
+        dp.distri_refresh_stale((wl.batch, wl.n_patches, 1, wl.n_patches, wl.patch), 2 * wl.groups,
+                                self.fm, self.table)
+
+    def layer(self, ev=None):
+        self.groupnorm()
+        self.conv()
+        if ev is not None:
+            ev[0].record()
+        self.attention()
+        if ev is not None:
+            ev[1].record()
+        self.refresh()
+
+
+def time_op(fn, iters, warmup=3):
+    import torch
+
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(iters)]
+    for k, (a, b) in enumerate(evs):
+        a.record()
+        fn(k + 1)
+        b.record()
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    return ts[len(ts) // 2], ts[0]
+
+
+def per_op(levels, iters):
+    """Median per-op times; GroupNorm and refresh rotate through > 512 MB."""
+    import torch
+
+    res = {}
+    for lv in levels:
+        wl = lv.wl
+        key = wl.name
+        slice_bytes = wl.slice_bytes()
+        nrot = max(2, int(math.ceil(600e6 / (2 * slice_bytes))))
+        xs = [torch.randn_like(lv.t["x_fresh"], dtype=torch.float32).to(torch.bfloat16) for _ in range(nrot)]
+        ys = [torch.empty_like(lv.t["x_fresh"]) for _ in range(nrot)]
+        gn_med, gn_min = time_op(lambda k: lv.groupnorm(xs[k % nrot], ys[k % nrot]), iters)
+        # refresh of the conv-input map, rotating fresh slices and stale maps
+        nrot_r = max(2, int(math.ceil(600e6 / (2 * slice_bytes + slice_bytes))))
+        stales = [torch.empty(wl.batch, wl.height, wl.width, wl.channels, dtype=torch.bfloat16,
+                              device="cuda") for _ in range(min(nrot_r, 8))]
+        nr = len(stales)
+        import displaced_patch_parallelism_distri_amd as dp
+
+        rf_med, rf_min = time_op(lambda k: dp.distri_refresh_stale(
+            lv.geom, wl.width * wl.channels, xs[k % nrot], stales[k % nr]), iters)
+        del xs, ys, stales
+        cv_med, cv_min = time_op(lambda k: lv.conv(), iters)
+        at_med, at_min = time_op(lambda k: lv.attention(), iters)
+        res[key] = {
+            "groupnorm_ms": gn_med, "groupnorm_gbps": 2 * slice_bytes / gn_med / 1e6,
+            "refresh_ms": rf_med, "refresh_gbps": 2 * slice_bytes / rf_med / 1e6,
+            "conv_ms": cv_med, "conv_tflops": wl.conv_flops() / cv_med / 1e9,
+            "attention_ms": at_med, "attention_tflops": wl.attn_flops() / at_med / 1e9,
+        }
+        torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(budget_s):
+    """The CPU oracle on a bounded sample of level (a): a few query rows of
+    attention (all images and heads, all 57600 keys) and one output row of the
+    conv; the rate is (sample FLOPs) / (oracle wall time)."""
+    import oracle
+    import synthetic_inputs as si
+    import torch
+
+    wl = si.WORKLOADS["sdxl3840_l2"].with_patch(4)
+    d = si.make_inputs(wl, device="cpu", nonzero_bias=True)
+    scale = wl.head_dim ** -0.5
+    # calibrate on 1 row, then scale to the budget
+    t0 = time.perf_counter()
+    oracle.patch_self_attn(wl.geom, wl.heads, 64, scale, d["q"], d["k_fresh"], d["v_fresh"],
+                           d["k_stale"], d["v_stale"], rows=(0, 1))
+    t1 = time.perf_counter() - t0
+    rows = max(1, min(wl.lq, int(0.8 * budget_s / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.patch_self_attn(wl.geom, wl.heads, 64, scale, d["q"], d["k_fresh"], d["v_fresh"],
+                           d["k_stale"], d["v_stale"], rows=(0, rows))
+    ta = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, d["x_fresh"], d["x_stale"],
+                              d["weight"], d["bias"], rows=(0, 1))
+    tc = time.perf_counter() - t0
+    fa = 4.0 * wl.batch * wl.heads * rows * wl.tokens * wl.head_dim
+    fc = 2.0 * wl.batch * wl.width * wl.channels * wl.channels * 9
+    return {"value": (fa + fc) / (ta + tc) / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"sdxl3840 level (a) patch 4: attention for {rows} local query rows x 2 images "
+                      f"x 10 heads over 57600 keys + conv for 1 output row (2 x 240 px x 640 ch), fp64; "
+                      f"{ta + tc:.1f} s",
+            "seconds": ta + tc}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU exchange is a design note, not part of this build)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import displaced_patch_parallelism_distri_amd as dp
+
+    dp.load()
+    dev = torch.device("cuda:0")
+    levels = [Level(n, args.patch, dev) for n in LEVELS]
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    for _ in range(args.warmup):
+        for lv in levels:
+            lv.layer()
+    torch.cuda.synchronize()
+    attn_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    layer_ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        layer_ev[k][0].record()
+        levels[0].layer(attn_ev[k])
+        layer_ev[k][1].record()
+        levels[1].layer()
+        layer_ev[k][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = wall * 1e3 / args.steps
+    la = sorted(e[0].elapsed_time(e[1]) for e in layer_ev)
+    lb = sorted(e[1].elapsed_time(e[2]) for e in layer_ev)
+    attn_ms = sum(a.elapsed_time(b) for a, b in attn_ev) / args.steps
+
+    flops = sum(lv.wl.attn_flops() + lv.wl.conv_flops() for lv in levels)
+    value = flops / (step_ms * 1e-3) / 1e12
+    ops = per_op(levels, args.op_iters)
+
+    wa = levels[0].wl
+    achieved = wa.attn_flops() / (attn_ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations of SDXL feature-map shape; no weights, no COCO)",
+        "config": {"workload": "sdxl3840 n=8 patch %d: (a) 2x640x240x240 10 heads + (b) 2x1280x120x120 "
+                               "20 heads; GN 32 groups, conv 3x3 C->C, attention d=64" % args.patch,
+                   "n_patches": 8, "patch": args.patch},
+        "ms_per_layer": {"sdxl3840_l2": round(la[len(la) // 2], 4), "sdxl3840_l3": round(lb[len(lb) // 2], 4)},
+        "per_op": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
+        "groupnorm_gbps": {k: round(v["groupnorm_gbps"], 1) for k, v in ops.items()},
+        "roofline": {"kernel": "attn_bf16_kernel (level a)", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(attn_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

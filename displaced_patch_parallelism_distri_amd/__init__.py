@@ -1,0 +1,234 @@
+"""Python binding of the gfx950 patch-layer library (``libdistri_patch.so``).
+
+One device's share of a DistriFusion patch layer under displaced patch
+parallelism: patch self-attention over fresh + stale K/V, the 3x3 conv with a
+stale halo, the corrected asynchronous GroupNorm and the stale refresh.  The
+functions here only marshal torch tensors (device memory and the current HIP
+stream) into the C ABI declared in ``include/distri_patch.h``; every step of
+the computation runs in the library's HIP kernels.  There is no fallback: if
+the library is missing or the call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "DistriError", "load", "abi_version", "geom",
+    "distri_patch_self_attn", "distri_patch_conv3x3_halo", "distri_async_groupnorm",
+    "distri_refresh_stale", "distri_patch_self_attn_workspace_size",
+    "distri_async_groupnorm_workspace_size",
+    "DISTRI_F32", "DISTRI_BF16",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdistri_patch.so")
+
+DISTRI_F32, DISTRI_BF16 = 0, 1
+STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
+          5: "ERR_UNSUPPORTED", 6: "ERR_WORKSPACE", 7: "ERR_HIP", 8: "ERR_ALIAS"}
+SYMBOLS = ("distri_abi_version", "distri_status_str", "distri_last_error",
+           "distri_patch_self_attn_workspace_size", "distri_patch_self_attn",
+           "distri_patch_conv3x3_halo", "distri_async_groupnorm_workspace_size",
+           "distri_async_groupnorm", "distri_refresh_stale")
+
+
+class DistriError(RuntimeError):
+    def __init__(self, status, func, detail):
+        self.status = status
+        super().__init__(f"{func}: {STATUS.get(status, status)} ({detail})")
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("height", ctypes.c_int64), ("width", ctypes.c_int64),
+                ("n_patches", ctypes.c_int64), ("patch", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load():
+    """Load libdistri_patch.so (built by ``python -m displaced_patch_parallelism_distri_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m displaced_patch_parallelism_distri_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    G = ctypes.POINTER(Geom)
+    lib.distri_abi_version.restype = I
+    lib.distri_status_str.restype = ctypes.c_char_p
+    lib.distri_status_str.argtypes = [I]
+    lib.distri_last_error.restype = ctypes.c_char_p
+    lib.distri_patch_self_attn_workspace_size.argtypes = [G, I64, I64, I, ctypes.POINTER(SZ)]
+    lib.distri_patch_self_attn.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 7 + [SZ, P]
+    lib.distri_patch_conv3x3_halo.argtypes = [G, I64, I64, I] + [P] * 5 + [P]
+    lib.distri_async_groupnorm_workspace_size.argtypes = [G, I64, I64, I, ctypes.POINTER(SZ)]
+    lib.distri_async_groupnorm.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 7 + [SZ, P]
+    lib.distri_refresh_stale.argtypes = [G, I64, I, P, P, P]
+    for name in SYMBOLS[3:]:
+        getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return int(load().distri_abi_version())
+
+
+def geom(batch, height, width, n_patches, patch) -> Geom:
+    return Geom(int(batch), int(height), int(width), int(n_patches), int(patch))
+
+
+def _as_geom(g):
+    return g if isinstance(g, Geom) else geom(*g)
+
+
+def _check(status, func):
+    if status != 0:
+        detail = load().distri_last_error().decode(errors="replace")
+        raise DistriError(status, func, detail)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DISTRI_BF16
+    if t.dtype == torch.float32:
+        return DISTRI_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t, name, dtype=None, numel=None):
+    """Device pointer of a dense tensor (or 0 for None)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.numel() > 0 and not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def distri_patch_self_attn_workspace_size(g, heads, head_dim, dtype_code) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().distri_patch_self_attn_workspace_size(ctypes.byref(_as_geom(g)), heads,
+                                                        head_dim, dtype_code, ctypes.byref(n)),
+           "distri_patch_self_attn_workspace_size")
+    return int(n.value)
+
+
+def distri_async_groupnorm_workspace_size(g, channels, groups, dtype_code) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().distri_async_groupnorm_workspace_size(ctypes.byref(_as_geom(g)), channels,
+                                                        groups, dtype_code, ctypes.byref(n)),
+           "distri_async_groupnorm_workspace_size")
+    return int(n.value)
+
+
+def _workspace(nbytes, ref, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=ref.device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def distri_patch_self_attn(g, heads, q, k_fresh, v_fresh, k_stale, v_stale, out=None,
+                           scale=None, head_dim=64, workspace=None, stream=None):
+    """Attention of patch i: q/k_fresh/v_fresh [B, Lq, heads, d], k_stale/v_stale
+    [B, L, heads, d] -> out [B, Lq, heads, d] (same dtype)."""
+    g = _as_geom(g)
+    code = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = head_dim ** -0.5
+    lq = (g.height // max(g.n_patches, 1)) * g.width
+    nl = g.batch * lq * heads * head_dim
+    nf = g.batch * g.height * g.width * heads * head_dim
+    ws_bytes = distri_patch_self_attn_workspace_size(g, heads, head_dim, code)
+    ws, ws_len = _workspace(ws_bytes, q, workspace)
+    st = load().distri_patch_self_attn(
+        ctypes.byref(g), heads, head_dim, float(scale), code,
+        _ptr(q, "q", q.dtype, nl), _ptr(k_fresh, "k_fresh", q.dtype, nl),
+        _ptr(v_fresh, "v_fresh", q.dtype, nl), _ptr(k_stale, "k_stale", q.dtype, nf),
+        _ptr(v_stale, "v_stale", q.dtype, nf), _ptr(out, "out", q.dtype, nl),
+        _ptr(ws, "workspace"), ws_len, _stream(stream))
+    _check(st, "distri_patch_self_attn")
+    return out
+
+
+def distri_patch_conv3x3_halo(g, x_fresh, x_stale, weight, bias=None, y=None, stream=None):
+    """3x3 conv of patch i: x_fresh [B,h,W,Cin], x_stale [B,H,W,Cin], weight
+    [Cout,3,3,Cin], bias [Cout] fp32 or None -> y [B,h,W,Cout]."""
+    g = _as_geom(g)
+    code = _dtype_code(x_fresh)
+    cout, cin = weight.shape[0], weight.shape[-1]
+    h = g.height // max(g.n_patches, 1)
+    if y is None:
+        y = torch.empty((g.batch, h, g.width, cout), dtype=x_fresh.dtype, device=x_fresh.device)
+    st = load().distri_patch_conv3x3_halo(
+        ctypes.byref(g), cin, cout, code,
+        _ptr(x_fresh, "x_fresh", x_fresh.dtype, g.batch * h * g.width * cin),
+        _ptr(x_stale, "x_stale", x_fresh.dtype, g.batch * g.height * g.width * cin),
+        _ptr(weight, "weight", x_fresh.dtype, cout * 9 * cin),
+        _ptr(bias, "bias", torch.float32, cout), _ptr(y, "y", x_fresh.dtype), _stream(stream))
+    _check(st, "distri_patch_conv3x3_halo")
+    return y
+
+
+def distri_async_groupnorm(g, groups, x_fresh, stale_moments, gamma=None, beta=None, eps=1e-5,
+                           y=None, fresh_moments=None, workspace=None, stream=None):
+    """Corrected async GroupNorm of patch i: x_fresh [B,h,W,C], stale_moments
+    [B,n,G,2] fp32 -> (y [B,h,W,C], fresh_moments [B,G,2] fp32)."""
+    g = _as_geom(g)
+    code = _dtype_code(x_fresh)
+    C = x_fresh.shape[-1]
+    if y is None:
+        y = torch.empty_like(x_fresh)
+    if fresh_moments is None:
+        fresh_moments = torch.empty((g.batch, groups, 2), dtype=torch.float32, device=x_fresh.device)
+    ws_bytes = distri_async_groupnorm_workspace_size(g, C, groups, code)
+    ws, ws_len = _workspace(ws_bytes, x_fresh, workspace)
+    st = load().distri_async_groupnorm(
+        ctypes.byref(g), C, groups, float(eps), code, _ptr(x_fresh, "x_fresh", x_fresh.dtype),
+        _ptr(stale_moments, "stale_moments", torch.float32, g.batch * g.n_patches * groups * 2),
+        _ptr(gamma, "gamma", torch.float32, C), _ptr(beta, "beta", torch.float32, C),
+        _ptr(y, "y", x_fresh.dtype, x_fresh.numel()),
+        _ptr(fresh_moments, "fresh_moments", torch.float32, g.batch * groups * 2),
+        _ptr(ws, "workspace"), ws_len, _stream(stream))
+    _check(st, "distri_async_groupnorm")
+    return y, fresh_moments
+
+
+def distri_refresh_stale(g, row_elems, fresh, stale, stream=None):
+    """stale[b, i*h + r, :] = fresh[b, r, :] in place; returns stale."""
+    g = _as_geom(g)
+    code = _dtype_code(fresh)
+    h = g.height // max(g.n_patches, 1)
+    st = load().distri_refresh_stale(
+        ctypes.byref(g), row_elems, code,
+        _ptr(fresh, "fresh", fresh.dtype, g.batch * h * row_elems),
+        _ptr(stale, "stale", fresh.dtype, g.batch * g.height * row_elems), _stream(stream))
+    _check(st, "distri_refresh_stale")
+    return stale

@@ -1,0 +1,270 @@
+// C ABI of the patch-layer library: host-side argument validation and
+// dispatch to the gfx950 kernels.  Every check runs before any HIP call, so a
+// rejected call enqueues nothing and touches no device state.
+#include "../../include/distri_patch.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+
+#include "dp_common.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int fail(int status, const char* fmt, const char* what) {
+    std::snprintf(g_last_error, sizeof(g_last_error), fmt, what);
+    return status;
+}
+
+#define DP_CHECK(cond, status, msg)                       \
+    do {                                                  \
+        if (!(cond)) return fail((status), "%s", (msg)); \
+    } while (0)
+
+int elem_bytes_of(int dtype) { return dtype == DISTRI_F32 ? 4 : 2; }
+
+// Geometry rules shared by every call.
+int check_geom(const distri_patch_geom* g) {
+    DP_CHECK(g != nullptr, DISTRI_ERR_NULL, "geometry pointer is NULL");
+    DP_CHECK(g->batch >= 0 && g->height >= 0 && g->width >= 0, DISTRI_ERR_SHAPE,
+             "batch, height and width must be >= 0");
+    DP_CHECK(g->n_patches >= 1, DISTRI_ERR_SHAPE, "n_patches must be >= 1");
+    DP_CHECK(g->patch >= 0 && g->patch < g->n_patches, DISTRI_ERR_SHAPE,
+             "patch must lie in [0, n_patches)");
+    DP_CHECK(g->height % g->n_patches == 0, DISTRI_ERR_SHAPE,
+             "height must be a multiple of n_patches");
+    DP_CHECK(g->batch <= 65535, DISTRI_ERR_UNSUPPORTED, "batch above 65535");
+    // keep every element offset far from int64 overflow
+    DP_CHECK(g->height <= (int64_t(1) << 24) && g->width <= (int64_t(1) << 24), DISTRI_ERR_UNSUPPORTED,
+             "height or width above 2^24");
+    return DISTRI_OK;
+}
+
+int check_dtype(int dtype) {
+    DP_CHECK(dtype == DISTRI_F32 || dtype == DISTRI_BF16, DISTRI_ERR_DTYPE,
+             "dtype must be DISTRI_F32 or DISTRI_BF16");
+    return DISTRI_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Range {
+    const void* p;
+    size_t bytes;
+};
+bool overlaps(Range a, Range b) {
+    if (a.bytes == 0 || b.bytes == 0 || a.p == nullptr || b.p == nullptr) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+dp::Geom to_geom(const distri_patch_geom* g) {
+    return dp::Geom{g->batch, g->height, g->width, g->n_patches, g->patch};
+}
+
+int hip_status(hipError_t e) {
+    if (e == hipSuccess) return DISTRI_OK;
+    std::snprintf(g_last_error, sizeof(g_last_error), "HIP error: %s", hipGetErrorString(e));
+    return DISTRI_ERR_HIP;
+}
+
+int check_attn_shape(const distri_patch_geom* g, int64_t heads, int64_t head_dim, int dtype) {
+    int st = check_geom(g);
+    if (st) return st;
+    st = check_dtype(dtype);
+    if (st) return st;
+    DP_CHECK(heads >= 1 && head_dim >= 1, DISTRI_ERR_SHAPE, "heads and head_dim must be >= 1");
+    DP_CHECK(heads <= 65535 / (g->batch > 0 ? g->batch : 1), DISTRI_ERR_UNSUPPORTED,
+             "batch * heads above 65535");
+    DP_CHECK(head_dim == 64, DISTRI_ERR_UNSUPPORTED, "head_dim must be 64");
+    return DISTRI_OK;
+}
+
+int check_gn_shape(const distri_patch_geom* g, int64_t C, int64_t G, int dtype) {
+    int st = check_geom(g);
+    if (st) return st;
+    st = check_dtype(dtype);
+    if (st) return st;
+    DP_CHECK(C >= 1 && G >= 1 && C % G == 0, DISTRI_ERR_SHAPE,
+             "channels and groups must be >= 1 with channels % groups == 0");
+    const int vec = 16 / elem_bytes_of(dtype);
+    DP_CHECK(C % vec == 0, DISTRI_ERR_UNSUPPORTED,
+             "channels must be a multiple of 8 (bf16) or 4 (fp32)");
+    DP_CHECK(C / vec <= 1024, DISTRI_ERR_UNSUPPORTED, "channels above 8192 (bf16) / 4096 (fp32)");
+    return DISTRI_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int distri_abi_version(void) { return DISTRI_PATCH_ABI_VERSION; }
+
+const char* distri_status_str(int status) {
+    switch (status) {
+        case DISTRI_OK: return "ok";
+        case DISTRI_ERR_NULL: return "null pointer";
+        case DISTRI_ERR_SHAPE: return "invalid shape";
+        case DISTRI_ERR_DTYPE: return "invalid dtype";
+        case DISTRI_ERR_ALIGN: return "misaligned pointer";
+        case DISTRI_ERR_UNSUPPORTED: return "unsupported configuration";
+        case DISTRI_ERR_WORKSPACE: return "workspace missing or too small";
+        case DISTRI_ERR_HIP: return "HIP runtime error";
+        case DISTRI_ERR_ALIAS: return "output overlaps an input";
+        default: return "unknown status";
+    }
+}
+
+const char* distri_last_error(void) { return g_last_error; }
+
+int distri_patch_self_attn_workspace_size(const distri_patch_geom* g, int64_t heads,
+                                          int64_t head_dim, int dtype, size_t* bytes) {
+    DP_CHECK(bytes != nullptr, DISTRI_ERR_NULL, "bytes pointer is NULL");
+    int st = check_attn_shape(g, heads, head_dim, dtype);
+    if (st) return st;
+    *bytes = dp::attention_workspace_bytes(to_geom(g), heads, dtype == DISTRI_BF16);
+    return DISTRI_OK;
+}
+
+int distri_patch_self_attn(const distri_patch_geom* g, int64_t heads, int64_t head_dim,
+                           float scale, int dtype, const void* q, const void* k_fresh,
+                           const void* v_fresh, const void* k_stale, const void* v_stale,
+                           void* out, void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_attn_shape(g, heads, head_dim, dtype);
+    if (st) return st;
+    DP_CHECK(std::isfinite(scale) && scale > 0.f, DISTRI_ERR_SHAPE, "scale must be finite and > 0");
+    const dp::Geom gg = to_geom(g);
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t local = size_t(gg.B * gg.lq() * heads * head_dim) * eb;
+    const size_t full = size_t(gg.B * gg.L() * heads * head_dim) * eb;
+    if (local == 0) return DISTRI_OK;
+    DP_CHECK(q && k_fresh && v_fresh && k_stale && v_stale && out, DISTRI_ERR_NULL,
+             "a tensor pointer is NULL");
+    DP_CHECK(aligned16(q) && aligned16(k_fresh) && aligned16(v_fresh) && aligned16(k_stale) &&
+                 aligned16(v_stale) && aligned16(out),
+             DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const Range o{out, local};
+    DP_CHECK(!overlaps(o, {q, local}) && !overlaps(o, {k_fresh, local}) &&
+                 !overlaps(o, {v_fresh, local}) && !overlaps(o, {k_stale, full}) &&
+                 !overlaps(o, {v_stale, full}),
+             DISTRI_ERR_ALIAS, "out overlaps an input");
+    const size_t need = dp::attention_workspace_bytes(gg, heads, dtype == DISTRI_BF16);
+    if (need > 0) {
+        DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
+                 "attention workspace missing or too small");
+        DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
+        DP_CHECK(!overlaps({workspace, need}, o), DISTRI_ERR_ALIAS, "workspace overlaps out");
+    }
+    return hip_status(dp::launch_attention(gg, heads, scale, dtype == DISTRI_BF16, q, k_fresh,
+                                           v_fresh, k_stale, v_stale, out, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int distri_patch_conv3x3_halo(const distri_patch_geom* g, int64_t c_in, int64_t c_out,
+                              int dtype, const void* x_fresh, const void* x_stale,
+                              const void* weight, const float* bias, void* y, void* stream) {
+    int st = check_geom(g);
+    if (st) return st;
+    st = check_dtype(dtype);
+    if (st) return st;
+    DP_CHECK(c_in >= 1 && c_out >= 1, DISTRI_ERR_SHAPE, "c_in and c_out must be >= 1");
+    DP_CHECK(c_in <= 65536 && c_out <= 65536, DISTRI_ERR_UNSUPPORTED, "channels above 65536");
+    if (dtype == DISTRI_BF16)
+        DP_CHECK(c_in % 32 == 0, DISTRI_ERR_UNSUPPORTED, "bf16 conv needs c_in % 32 == 0");
+    const dp::Geom gg = to_geom(g);
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t ybytes = size_t(gg.B * gg.h() * gg.W * c_out) * eb;
+    if (ybytes == 0) return DISTRI_OK;
+    const size_t xf_bytes = size_t(gg.B * gg.h() * gg.W * c_in) * eb;
+    const size_t xs_bytes = size_t(gg.B * gg.H * gg.W * c_in) * eb;
+    const size_t w_bytes = size_t(c_out * 9 * c_in) * eb;
+    const bool need_stale = gg.n > 1;
+    DP_CHECK(x_fresh && weight && y && (x_stale || !need_stale), DISTRI_ERR_NULL,
+             "a tensor pointer is NULL");
+    DP_CHECK(aligned16(x_fresh) && aligned16(x_stale) && aligned16(weight) && aligned16(y) &&
+                 aligned16(bias),
+             DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const Range o{y, ybytes};
+    DP_CHECK(!overlaps(o, {x_fresh, xf_bytes}) && !overlaps(o, {x_stale, xs_bytes}) &&
+                 !overlaps(o, {weight, w_bytes}) &&
+                 !overlaps(o, {bias, bias ? size_t(c_out) * 4 : 0}),
+             DISTRI_ERR_ALIAS, "y overlaps an input");
+    return hip_status(dp::launch_conv3x3(gg, c_in, c_out, dtype == DISTRI_BF16, x_fresh, x_stale,
+                                         weight, bias, y, static_cast<hipStream_t>(stream)));
+}
+
+int distri_async_groupnorm_workspace_size(const distri_patch_geom* g, int64_t channels,
+                                          int64_t groups, int dtype, size_t* bytes) {
+    DP_CHECK(bytes != nullptr, DISTRI_ERR_NULL, "bytes pointer is NULL");
+    int st = check_gn_shape(g, channels, groups, dtype);
+    if (st) return st;
+    *bytes = dp::groupnorm_workspace_bytes(to_geom(g), channels, groups, elem_bytes_of(dtype));
+    return DISTRI_OK;
+}
+
+int distri_async_groupnorm(const distri_patch_geom* g, int64_t channels, int64_t groups,
+                           float eps, int dtype, const void* x_fresh,
+                           const float* stale_moments, const float* gamma, const float* beta,
+                           void* y, float* fresh_moments, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    int st = check_gn_shape(g, channels, groups, dtype);
+    if (st) return st;
+    DP_CHECK(std::isfinite(eps) && eps >= 0.f, DISTRI_ERR_SHAPE, "eps must be finite and >= 0");
+    const dp::Geom gg = to_geom(g);
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t xbytes = size_t(gg.B * gg.h() * gg.W * channels) * eb;
+    if (xbytes == 0) return DISTRI_OK;
+    DP_CHECK(x_fresh && stale_moments && y && fresh_moments, DISTRI_ERR_NULL,
+             "a tensor pointer is NULL");
+    DP_CHECK(aligned16(x_fresh) && aligned16(stale_moments) && aligned16(gamma) &&
+                 aligned16(beta) && aligned16(y) && aligned16(fresh_moments),
+             DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const size_t need = dp::groupnorm_workspace_bytes(gg, channels, groups, int(eb));
+    DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
+             "groupnorm workspace missing or too small");
+    DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t table = size_t(gg.B * gg.n * groups * 2) * 4;
+    const size_t fm = size_t(gg.B * groups * 2) * 4;
+    const size_t cb = size_t(channels) * 4;
+    const Range outs[3] = {{y, xbytes}, {fresh_moments, fm}, {workspace, need}};
+    const Range ins[4] = {{x_fresh, xbytes}, {stale_moments, table}, {gamma, gamma ? cb : 0},
+                          {beta, beta ? cb : 0}};
+    for (const Range& o : outs)
+        for (const Range& in : ins)
+            DP_CHECK(!overlaps(o, in), DISTRI_ERR_ALIAS, "an output overlaps an input");
+    DP_CHECK(!overlaps(outs[0], outs[1]) && !overlaps(outs[0], outs[2]) &&
+                 !overlaps(outs[1], outs[2]),
+             DISTRI_ERR_ALIAS, "outputs overlap each other");
+    return hip_status(dp::launch_groupnorm(gg, channels, groups, eps, dtype == DISTRI_BF16,
+                                           x_fresh, stale_moments, gamma, beta, y, fresh_moments,
+                                           workspace, static_cast<hipStream_t>(stream)));
+}
+
+int distri_refresh_stale(const distri_patch_geom* g, int64_t row_elems, int dtype,
+                         const void* fresh, void* stale, void* stream) {
+    int st = check_geom(g);
+    if (st) return st;
+    st = check_dtype(dtype);
+    if (st) return st;
+    DP_CHECK(row_elems >= 0, DISTRI_ERR_SHAPE, "row_elems must be >= 0");
+    DP_CHECK(row_elems <= (int64_t(1) << 32), DISTRI_ERR_UNSUPPORTED, "row_elems above 2^32");
+    const dp::Geom gg = to_geom(g);
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t fbytes = size_t(gg.B * gg.h() * row_elems) * eb;
+    if (fbytes == 0) return DISTRI_OK;
+    DP_CHECK(fresh && stale, DISTRI_ERR_NULL, "a tensor pointer is NULL");
+    DP_CHECK((reinterpret_cast<uintptr_t>(fresh) % eb) == 0 &&
+                 (reinterpret_cast<uintptr_t>(stale) % eb) == 0,
+             DISTRI_ERR_ALIGN, "pointers must be aligned to the element size");
+    const size_t sbytes = size_t(gg.B * gg.H * row_elems) * eb;
+    DP_CHECK(!overlaps({stale, sbytes}, {fresh, fbytes}), DISTRI_ERR_ALIAS,
+             "stale overlaps fresh");
+    return hip_status(dp::launch_refresh(gg, row_elems, int(eb), fresh, stale,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

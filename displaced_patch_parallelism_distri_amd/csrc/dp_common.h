@@ -1,0 +1,102 @@
+// Shared device-side helpers and the internal launcher interface of the
+// gfx950 patch-layer library.  Internal to the HIP library; not part of the
+// C ABI (include/distri_patch.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// bf16 <-> fp32.  Widening is exact; narrowing is round-to-nearest-even
+// (the compiler emits v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(uint32_t(b) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v;
+    v.x = (__bf16)lo;
+    v.y = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Element-type traits for the two storage dtypes: a 16-byte vector holds
+// VEC elements.
+struct Bf16T {
+    typedef uint16_t elem;
+    static constexpr int VEC = 8;
+    __device__ static float to_f32(elem e) { return bf16_to_f32(e); }
+    __device__ static elem from_f32(float f) { return f32_to_bf16(f); }
+    __device__ static void unpack(const u32x4& v, float* out) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            out[2 * j] = __uint_as_float(v[j] << 16);
+            out[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+        }
+    }
+    __device__ static u32x4 pack(const float* in) {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = pack_bf16x2(in[2 * j], in[2 * j + 1]);
+        return v;
+    }
+};
+struct F32T {
+    typedef float elem;
+    static constexpr int VEC = 4;
+    __device__ static float to_f32(elem e) { return e; }
+    __device__ static elem from_f32(float f) { return f; }
+    __device__ static void unpack(const u32x4& v, float* out) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[j] = __uint_as_float(v[j]);
+    }
+    __device__ static u32x4 pack(const float* in) {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = __float_as_uint(in[j]);
+        return v;
+    }
+};
+
+__host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------------------
+// Internal launchers.  Arguments are already validated by the ABI layer.
+struct Geom {
+    int64_t B, H, W, n, i;
+    int64_t h() const { return H / n; }
+    int64_t lq() const { return (H / n) * W; }
+    int64_t L() const { return H * W; }
+};
+
+hipError_t launch_refresh(const Geom& g, int64_t row_elems, int elem_bytes, const void* fresh,
+                          void* stale, hipStream_t s);
+
+size_t groupnorm_workspace_bytes(const Geom& g, int64_t C, int64_t G, int elem_bytes);
+hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool bf16,
+                            const void* x, const float* stale_moments, const float* gamma,
+                            const float* beta, void* y, float* fresh_moments, void* ws,
+                            hipStream_t s);
+
+size_t attention_workspace_bytes(const Geom& g, int64_t heads, bool bf16);
+hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16, const void* q,
+                            const void* kf, const void* vf, const void* ks, const void* vs,
+                            void* out, void* ws, hipStream_t s);
+
+hipError_t launch_conv3x3(const Geom& g, int64_t cin, int64_t cout, bool bf16, const void* xf,
+                          const void* xs, const void* w, const float* bias, void* y,
+                          hipStream_t s);
+
+}  // namespace dp

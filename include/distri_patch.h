@@ -1,0 +1,176 @@
+/*
+ * distri_patch.h - C ABI of the MI355X (gfx950) library for one device's
+ * share of a DistriFusion patch layer under displaced patch parallelism.
+ *
+ * The method (DistriFusion, "Distributed Parallel Inference for
+ * High-Resolution Diffusion Models") splits the latent image into row
+ * patches, one per device.  After the first synchronous steps each device
+ * computes its own patch with fresh activations and takes the context of the
+ * other patches from the previous denoising step, exchanged asynchronously
+ * ("DistriFusion：高分辨率扩散模型的分布式并行推理", dongaigc.com mirror of the
+ * project README, section 概述, figure (c); meens.ai catalog page, section 2).
+ * The layers it wraps are Conv2d, self-attention and GroupNorm
+ * ("DistriFusion源码探秘：从DistriUNetPP到DistriAttentionTP的模块设计原理",
+ * section "Patch Parallelism的实现原理", items 1-3).  This library holds the
+ * per-device arithmetic of those layers; on one GPU the other patches' stale
+ * activations are ordinary device memory.
+ *
+ * Geometry.  A full map has B images of H rows x W columns.  It is split into
+ * n row bands of h = H / n rows; patch i owns rows [i*h, (i+1)*h) and, as a
+ * token sequence (token = row * W + col), tokens [i*Lq, (i+1)*Lq) with
+ * Lq = h*W.  L = H*W is the full token count.
+ *
+ * Conventions shared by every entry point.
+ *  - All tensor pointers are DEVICE pointers owned by the caller, dense and
+ *    row-major with the layouts given per call.  The library allocates
+ *    nothing and keeps no state between calls.
+ *  - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *    default stream).  Calls return without synchronising; results are ready
+ *    when the stream reaches that point.  Calls are thread-safe.
+ *  - Outputs must not overlap inputs (DISTRI_ERR_ALIAS).
+ *  - Every argument is validated on the host before any HIP call; a bad
+ *    argument returns its status code with nothing enqueued.  A call whose
+ *    output has no elements returns DISTRI_OK without touching the GPU (its
+ *    pointers may then be NULL).  A failed launch returns DISTRI_ERR_HIP.
+ *  - Tensor pointers must be 16-byte aligned (DISTRI_ERR_ALIGN), except for
+ *    distri_refresh_stale, which needs only element alignment.
+ *  - bf16 values are IEEE-754 binary32 truncated to the top 16 bits; every
+ *    kernel rounds its fp32 results to bf16 with round-to-nearest-even.
+ *  - distri_last_error() returns a thread-local text naming the argument
+ *    that the last failing call on this thread rejected.
+ */
+#ifndef DISTRI_PATCH_H
+#define DISTRI_PATCH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DISTRI_PATCH_ABI_VERSION 1
+
+typedef enum { DISTRI_F32 = 0, DISTRI_BF16 = 1 } distri_dtype;
+
+typedef enum {
+    DISTRI_OK = 0,
+    DISTRI_ERR_NULL = 1,        /* a required pointer is NULL */
+    DISTRI_ERR_SHAPE = 2,       /* inconsistent or out-of-range sizes */
+    DISTRI_ERR_DTYPE = 3,       /* dtype not one of distri_dtype */
+    DISTRI_ERR_ALIGN = 4,       /* pointer not aligned as required */
+    DISTRI_ERR_UNSUPPORTED = 5, /* valid, but outside what the kernels handle */
+    DISTRI_ERR_WORKSPACE = 6,   /* workspace missing or too small */
+    DISTRI_ERR_HIP = 7,         /* the HIP runtime reported an error */
+    DISTRI_ERR_ALIAS = 8        /* an output overlaps an input */
+} distri_status;
+
+/* (B, H, W, n, i): batch, full-map rows, columns, patch count, this patch. */
+typedef struct {
+    int64_t batch, height, width, n_patches, patch;
+} distri_patch_geom;
+
+int distri_abi_version(void);
+const char *distri_status_str(int status);
+const char *distri_last_error(void);
+
+/*
+ * distri_patch_self_attn - self-attention of patch i over the fresh + stale
+ * token map (DistriSelfAttentionPP in the source walkthrough, section
+ * "Patch Parallelism的实现原理", item 2; stale context per the README
+ * mirror, section 概述, figure (c)).
+ *
+ * For every image b, head hd and local query row r:
+ *   out[b, r, hd, :] = sum_t softmax_t(scale * <q[b, r, hd, :], K^[b, t, hd, :]>) V^[b, t, hd, :]
+ * over all L tokens t, where K^/V^ row t is k_fresh/v_fresh[b, t - i*Lq] for
+ * t in [i*Lq, (i+1)*Lq) and k_stale/v_stale[b, t] otherwise.  No mask.  The
+ * stale maps' rows of patch i are never read.
+ *
+ *   q, k_fresh, v_fresh, out   [B, Lq, heads, head_dim]   dtype
+ *   k_stale, v_stale           [B, L,  heads, head_dim]   dtype
+ *   scale                      finite (1/sqrt(head_dim) for SDXL)
+ *   workspace                  >= distri_patch_self_attn_workspace_size()
+ *                              bytes of device memory (may be NULL if that
+ *                              size is 0); contents on entry are ignored.
+ * head_dim must be 64 (DISTRI_ERR_UNSUPPORTED otherwise).  bf16 inputs are
+ * computed with bf16 MFMA and fp32 accumulation / softmax; fp32 inputs in
+ * fp32 throughout.
+ */
+int distri_patch_self_attn_workspace_size(const distri_patch_geom *g, int64_t heads,
+                                          int64_t head_dim, int dtype, size_t *bytes);
+int distri_patch_self_attn(const distri_patch_geom *g, int64_t heads, int64_t head_dim,
+                           float scale, int dtype, const void *q, const void *k_fresh,
+                           const void *v_fresh, const void *k_stale, const void *v_stale,
+                           void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * distri_patch_conv3x3_halo - 3x3 convolution (stride 1, zero padding 1) of
+ * patch i (DistriConv2dPP, source walkthrough, item 1).  The input rows just
+ * above and below the patch (the halo) come from the previous step's stale
+ * map: row i*h-1 if i > 0 and row (i+1)*h if i < n-1; outside the image the
+ * padding is zero.
+ *
+ *   y[b, r, c, o] = bias[o] + sum_{kh,kw,ci} w[o, kh, kw, ci] * X^[b, i*h+r+kh-1, c+kw-1, ci]
+ *
+ *   x_fresh  [B, h, W, Cin]       dtype  (NHWC)
+ *   x_stale  [B, H, W, Cin]       dtype  (only the two halo rows are read)
+ *   weight   [Cout, 3, 3, Cin]    dtype
+ *   bias     [Cout] fp32 or NULL
+ *   y        [B, h, W, Cout]      dtype
+ * bf16 requires Cin % 32 == 0 (DISTRI_ERR_UNSUPPORTED); any Cout.
+ */
+int distri_patch_conv3x3_halo(const distri_patch_geom *g, int64_t c_in, int64_t c_out,
+                              int dtype, const void *x_fresh, const void *x_stale,
+                              const void *weight, const float *bias, void *y, void *stream);
+
+/*
+ * distri_async_groupnorm - corrected asynchronous GroupNorm of patch i
+ * (DistriGroupNorm, source walkthrough, item 3; default sync mode per the
+ * README mirror's --sync_mode flag).  Per image b and group g (C/G
+ * consecutive channels):
+ *   m1, m2  = E[x], E[x^2] over this patch's h*W*(C/G) fresh values
+ *   mu      = (m1 + sum_{j != i} stale_moments[b, j, g, 0]) / n
+ *   e2      = (m2 + sum_{j != i} stale_moments[b, j, g, 1]) / n
+ *   rstd    = 1 / sqrt(max(e2 - mu^2, 0) + eps)
+ *   y       = (x - mu) * rstd * gamma[c] + beta[c]
+ *   fresh_moments[b, g, :] = (m1, m2)
+ * Slot i of stale_moments is never read.  With the other slots equal to the
+ * per-patch moments of the previous step's map this is GroupNorm of the
+ * hybrid map.
+ *
+ *   x_fresh, y      [B, h, W, C]  dtype (NHWC)
+ *   stale_moments   [B, n, G, 2]  fp32
+ *   gamma, beta     [C] fp32, or NULL for 1 and 0
+ *   fresh_moments   [B, G, 2]     fp32 (output)
+ *   workspace       >= distri_async_groupnorm_workspace_size() bytes;
+ *                   contents on entry are ignored
+ * C must be a multiple of 8 for bf16 and of 4 for fp32 (UNSUPPORTED).
+ */
+int distri_async_groupnorm_workspace_size(const distri_patch_geom *g, int64_t channels,
+                                          int64_t groups, int dtype, size_t *bytes);
+int distri_async_groupnorm(const distri_patch_geom *g, int64_t channels, int64_t groups,
+                           float eps, int dtype, const void *x_fresh,
+                           const float *stale_moments, const float *gamma, const float *beta,
+                           void *y, float *fresh_moments, void *workspace,
+                           size_t workspace_bytes, void *stream);
+
+/*
+ * distri_refresh_stale - make this step's fresh slice the next step's stale
+ * context (the reuse of the previous step's activations, README mirror,
+ * section 概述, figure (c)):
+ *   stale[b, i*h + r, :] = fresh[b, r, :]   for r in [0, h)
+ * Other rows of stale are left unchanged.  Bitwise copy.
+ *
+ *   fresh  [B, h, row_elems]   stale  [B, H, row_elems]   dtype
+ * K/V maps use row_elems = W*heads*head_dim, conv inputs W*C, and the
+ * GroupNorm moment table the geometry (B, n, 1, n, i) with row_elems = 2*G
+ * and DISTRI_F32.
+ */
+int distri_refresh_stale(const distri_patch_geom *g, int64_t row_elems, int dtype,
+                         const void *fresh, void *stale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DISTRI_PATCH_H */

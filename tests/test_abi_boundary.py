@@ -1,0 +1,148 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every entry point the header declares, and
+reject every invalid argument with its status code before any HIP call - so
+these calls are safe without a device: the fake pointers are never touched.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import displaced_patch_parallelism_distri_amd as dp
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "distri_patch.h")
+OK, NULL, SHAPE, DTYPE, ALIGN, UNSUP, WS, HIP, ALIAS = range(9)
+BF16, F32 = dp.DISTRI_BF16, dp.DISTRI_F32
+A = 0x7f0000000000  # a fake, 16-byte aligned "device" address, never dereferenced
+MB = 1 << 20
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dp.load()
+
+
+def G(*v):
+    return ctypes.byref(dp.geom(*v))
+
+
+def test_exports_every_declared_symbol(lib):
+    with open(HEADER) as f:
+        text = f.read()
+    declared = set(re.findall(r"^\s*(?:int|const char \*|size_t)\s*(distri_\w+)\s*\(", text, re.M))
+    assert declared == set(dp.SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert dp.abi_version() == 1
+    assert lib.distri_status_str(OK) == b"ok"
+    assert lib.distri_status_str(ALIAS) == b"output overlaps an input"
+    assert lib.distri_status_str(99) == b"unknown status"
+
+
+def attn(lib, geom, heads=10, hd=64, scale=0.125, dtype=BF16, ptrs=None, ws=None, wsb=0):
+    p = ptrs or [A + k * 64 * MB for k in range(6)]
+    return lib.distri_patch_self_attn(G(*geom), heads, hd, scale, dtype, *p, ws, wsb, None)
+
+
+def test_attention_rejects_bad_arguments(lib):
+    g = (2, 64, 64, 8, 3)
+    assert lib.distri_patch_self_attn(None, 10, 64, 0.125, BF16, *([A] * 6), None, 0, None) == NULL
+    assert attn(lib, (2, 65, 64, 8, 0)) == SHAPE          # H % n != 0
+    assert attn(lib, (2, 64, 64, 8, 8)) == SHAPE          # i >= n
+    assert attn(lib, (2, 64, 64, 0, 0)) == SHAPE          # n < 1
+    assert attn(lib, (-1, 64, 64, 8, 0)) == SHAPE
+    assert attn(lib, g, hd=128) == UNSUP                  # head_dim != 64
+    assert attn(lib, g, heads=0) == SHAPE
+    assert attn(lib, g, dtype=7) == DTYPE
+    assert attn(lib, g, scale=0.0) == SHAPE
+    assert attn(lib, g, scale=float("inf")) == SHAPE
+    p = [A + k * 64 * MB for k in range(6)]
+    p[2] = None
+    assert attn(lib, g, ptrs=p) == NULL
+    p = [A + k * 64 * MB for k in range(6)]
+    p[4] += 8
+    assert attn(lib, g, ptrs=p) == ALIGN
+    p = [A + k * 64 * MB for k in range(6)]
+    p[5] = p[3] + 1024                                   # out inside k_stale
+    assert attn(lib, g, ptrs=p) == ALIAS
+
+
+def test_attention_empty_output_is_ok_without_pointers(lib):
+    assert attn(lib, (0, 64, 64, 8, 0), ptrs=[None] * 6) == OK
+    assert attn(lib, (2, 0, 64, 8, 0), ptrs=[None] * 6) == OK
+
+
+def conv(lib, geom, cin=640, cout=640, dtype=BF16, ptrs=None, bias=None):
+    p = ptrs or [A + k * 256 * MB for k in range(4)]
+    return lib.distri_patch_conv3x3_halo(G(*geom), cin, cout, dtype, p[0], p[1], p[2], bias, p[3], None)
+
+
+def test_conv_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    assert conv(lib, (2, 241, 240, 8, 4)) == SHAPE
+    assert conv(lib, (2, 240, 240, 8, 9)) == SHAPE
+    assert conv(lib, g, cin=48) == UNSUP                  # bf16 needs c_in % 32
+    assert conv(lib, g, cin=0) == SHAPE
+    assert conv(lib, g, dtype=2) == DTYPE
+    assert conv(lib, g, ptrs=[A, None, A + 512 * MB, A + 768 * MB]) == NULL   # stale needed (n > 1)
+    assert conv(lib, g, ptrs=[A, A + 256 * MB, A + 512 * MB, A + 8]) == ALIGN
+    assert conv(lib, g, ptrs=[A, A + 256 * MB, A + 512 * MB, A + 16]) == ALIAS
+    assert conv(lib, g, bias=A + 4) == ALIGN
+    assert conv(lib, (0, 240, 240, 8, 4), ptrs=[None] * 4) == OK
+
+
+def test_groupnorm_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    n = ctypes.c_size_t(0)
+    assert lib.distri_async_groupnorm_workspace_size(G(*g), 640, 32, BF16, ctypes.byref(n)) == OK
+    assert n.value > 0
+    assert lib.distri_async_groupnorm_workspace_size(G(*g), 640, 33, BF16, ctypes.byref(n)) == SHAPE
+    assert lib.distri_async_groupnorm_workspace_size(G(*g), 644, 4, BF16, ctypes.byref(n)) == UNSUP
+    assert lib.distri_async_groupnorm_workspace_size(G(*g), 640, 32, BF16, None) == NULL
+    x, tab, gam, bet, y, fm, ws = (A + k * 64 * MB for k in range(7))
+
+    def call(geom=g, C=640, G_=32, eps=1e-5, dt=BF16, x=x, tab=tab, y=y, fm=fm, ws=ws, wsb=n.value):
+        return lib.distri_async_groupnorm(G(*geom), C, G_, eps, dt, x, tab, gam, bet, y, fm, ws, wsb, None)
+
+    lib.distri_async_groupnorm_workspace_size(G(*g), 640, 32, BF16, ctypes.byref(n))
+    assert call(eps=-1.0) == SHAPE
+    assert call(eps=float("nan")) == SHAPE
+    assert call(wsb=n.value - 1) == WS
+    assert call(ws=None) == WS
+    assert call(tab=None) == NULL
+    assert call(fm=A + 64 * MB * 5 + 4) == ALIGN
+    assert call(y=x + 1024) == ALIAS
+    assert call(ws=y + 16) == ALIAS
+    assert call(geom=(2, 240, 240, 7, 0)) == SHAPE
+    assert call(geom=(0, 240, 240, 8, 0), x=None, tab=None, y=None, fm=None, ws=None) == OK
+
+
+def test_refresh_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    f, s = A, A + 512 * MB
+    assert lib.distri_refresh_stale(G(*g), -1, BF16, f, s, None) == SHAPE
+    assert lib.distri_refresh_stale(G(*g), 100, 5, f, s, None) == DTYPE
+    assert lib.distri_refresh_stale(G(*g), 100, BF16, None, s, None) == NULL
+    assert lib.distri_refresh_stale(G(*g), 100, BF16, f + 1, s, None) == ALIGN
+    assert lib.distri_refresh_stale(G(*g), 100, F32, f + 2, s, None) == ALIGN
+    assert lib.distri_refresh_stale(G(*g), 100, BF16, f, f + 2, None) == ALIAS
+    assert lib.distri_refresh_stale(G(*(2, 240, 240, 8, 8)), 100, BF16, f, s, None) == SHAPE
+    assert lib.distri_refresh_stale(G(*g), 0, BF16, None, None, None) == OK
+
+
+def test_last_error_names_the_argument(lib):
+    attn(lib, (2, 64, 64, 8, 0), hd=32)
+    assert b"head_dim" in lib.distri_last_error()
+
+
+def test_python_binding_raises_on_cpu_tensors():
+    import torch
+
+    x = torch.zeros(2, 8, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        dp.distri_refresh_stale((2, 32, 8, 4, 0), 8 * 64, x, torch.zeros(2, 32, 8, 64, dtype=torch.bfloat16))

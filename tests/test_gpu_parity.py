@@ -1,0 +1,234 @@
+"""GPU parity: every op through the C ABI against the CPU oracle on the same
+seeded inputs (tolerances in tests/parity_util.py).
+
+Small workloads are compared element by element over the whole output; the
+2048^2 and 3840^2 workloads run the kernels at full size, in the launch
+configuration the benchmark times, and compare sampled output rows that the
+oracle computes one by one (first rows, a tile boundary, the ragged tail).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import displaced_patch_parallelism_distri_amd as dp
+import oracle
+import synthetic_inputs as si
+from tests.parity_util import assert_close, cpu_inputs, gpu_copy, sample_rows, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    dp.load()  # raises if the HIP library is missing
+
+
+W = si.WORKLOADS
+RAGGED_BF16 = si.Workload("ragged_bf16", 1, 128, 20, 13, 4, 2, seed=2024)     # Lq=65, L=260
+RAGGED_F32 = si.Workload("ragged_f32", 2, 64, 12, 7, 3, 1, dtype="f32", sigma=0.05, seed=2025)
+FULL_CASES = [(W["tiny"], 0), (W["tiny"], 1), (W["sdxl1024_l2"], 0), (W["sdxl1024_l2"], 3),
+              (W["sdxl1024_l2"], 7), (W["sdxl1024_l3"], 1), (W["sdxl1024_l3"], 3),
+              (RAGGED_BF16, 0), (RAGGED_BF16, 2), (RAGGED_BF16, 3), (RAGGED_F32, 1)]
+SAMPLED_CASES = [(W["sdxl2048_l2"], 4), (W["sdxl3840_l2"], 0), (W["sdxl3840_l2"], 4),
+                 (W["sdxl3840_l2"], 7), (W["sdxl3840_l3"], 4)]
+
+
+def _ids(cases):
+    return [f"{wl.name}-p{i}" for wl, i in cases]
+
+
+def _run_attention(wl, g):
+    return dp.distri_patch_self_attn(wl.geom, wl.heads, g["q"], g["k_fresh"], g["v_fresh"],
+                                     g["k_stale"], g["v_stale"], scale=wl.head_dim ** -0.5)
+
+
+def _oracle_attention(wl, d, rows=None):
+    return oracle.patch_self_attn(wl.geom, wl.heads, wl.head_dim, wl.head_dim ** -0.5, d["q"],
+                                  d["k_fresh"], d["v_fresh"], d["k_stale"], d["v_stale"], rows=rows)
+
+
+@pytest.mark.parametrize("wl,patch", FULL_CASES, ids=_ids(FULL_CASES))
+def test_all_ops_full_output(wl, patch):
+    wl = wl.with_patch(patch)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    tag = f"{wl.name} patch {patch}"
+
+    out = _run_attention(wl, g)
+    assert_close(to_np(out), _oracle_attention(wl, d), wl.dtype, f"attention {tag}")
+
+    y = dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], g["x_stale"], g["weight"], g["bias"])
+    ref = oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, d["x_fresh"], d["x_stale"],
+                                    d["weight"], d["bias"])
+    assert_close(to_np(y), ref, wl.dtype, f"conv {tag}")
+
+    yg, fm = dp.distri_async_groupnorm(wl.geom, wl.groups, g["x_fresh"], g["table"], g["gamma"],
+                                       g["beta"], eps=wl.eps)
+    ref_y, ref_fm = oracle.async_groupnorm(wl.geom, wl.channels, wl.groups, wl.eps, d["x_fresh"],
+                                           d["table"].double().numpy(), d["gamma"], d["beta"])
+    assert_close(to_np(yg), ref_y, wl.dtype, f"groupnorm {tag}")
+    fmn = to_np(fm)
+    assert np.all(np.abs(fmn[..., 0] - ref_fm[..., 0]) <= 1e-5 * np.sqrt(ref_fm[..., 1]) + 1e-7)
+    assert np.all(np.abs(fmn[..., 1] - ref_fm[..., 1]) <= 1e-5 * ref_fm[..., 1] + 1e-7)
+
+
+@pytest.mark.parametrize("wl,patch", SAMPLED_CASES, ids=_ids(SAMPLED_CASES))
+def test_full_size_sampled(wl, patch):
+    wl = wl.with_patch(patch)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    tag = f"{wl.name} patch {patch}"
+    out = to_np(_run_attention(wl, g))
+    for r0, r1 in sample_rows(wl.lq, 256, 4):
+        ref = _oracle_attention(wl, d, rows=(r0, r1))
+        assert_close(out[:, r0:r1], ref, wl.dtype, f"attention {tag} rows {r0}:{r1}")
+
+    y = to_np(dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], g["x_stale"], g["weight"], g["bias"]))
+    for r0, r1 in [(0, 1), (wl.h // 2, wl.h // 2 + 1), (wl.h - 1, wl.h)]:
+        ref = oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, d["x_fresh"], d["x_stale"],
+                                        d["weight"], d["bias"], rows=(r0, r1))
+        assert_close(y[:, r0:r1], ref, wl.dtype, f"conv {tag} rows {r0}:{r1}")
+
+    yg, fm = dp.distri_async_groupnorm(wl.geom, wl.groups, g["x_fresh"], g["table"], g["gamma"],
+                                       g["beta"], eps=wl.eps)
+    ref_y, ref_fm = oracle.async_groupnorm(wl.geom, wl.channels, wl.groups, wl.eps, d["x_fresh"],
+                                           d["table"].double().numpy(), d["gamma"], d["beta"])
+    assert_close(to_np(yg), ref_y, wl.dtype, f"groupnorm {tag}")
+    np.testing.assert_allclose(to_np(fm), ref_fm, rtol=1e-5, atol=1e-7)
+
+
+REFRESH_CASES = [(W["tiny"], 1), (W["sdxl1024_l2"], 5), (W["sdxl3840_l2"], 4), (RAGGED_BF16, 3)]
+
+
+@pytest.mark.parametrize("wl,patch", REFRESH_CASES, ids=_ids(REFRESH_CASES))
+def test_refresh_bitwise(wl, patch):
+    wl = wl.with_patch(patch)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    B, H, Wd, h = wl.batch, wl.height, wl.width, wl.h
+    tok_row = Wd * wl.heads * wl.head_dim
+    for fresh, stale, row in (("k_fresh", "k_stale", tok_row), ("v_fresh", "v_stale", tok_row),
+                              ("x_fresh", "x_stale", Wd * wl.channels)):
+        s = g[stale].clone()
+        dp.distri_refresh_stale(wl.geom, row, g[fresh], s)
+        ref = d[stale].clone()
+        ref.view(B, H, row)[:, patch * h:(patch + 1) * h] = d[fresh].view(B, h, row)
+        assert torch.equal(s.cpu().view(torch.int16 if s.dtype == torch.bfloat16 else torch.int32),
+                           ref.view(torch.int16 if s.dtype == torch.bfloat16 else torch.int32))
+    # the GroupNorm moment table: geometry (B, n, 1, n, i), 2G floats per row
+    tab = g["table"].clone()
+    fresh_m = torch.randn(B, wl.groups, 2).cuda()
+    dp.distri_refresh_stale((B, wl.n_patches, 1, wl.n_patches, patch), 2 * wl.groups, fresh_m, tab)
+    ref = d["table"].clone()
+    ref[:, patch] = fresh_m.cpu()
+    assert torch.equal(tab.cpu(), ref)
+
+
+def test_refresh_odd_rows_and_alignment():
+    """Rows whose byte size is not a multiple of 16 (scalar path)."""
+    geom = (3, 6, 1, 3, 1)
+    fresh = torch.arange(3 * 2 * 5, dtype=torch.bfloat16).cuda()
+    stale = torch.full((3 * 6 * 5,), -1.0, dtype=torch.bfloat16).cuda()
+    dp.distri_refresh_stale(geom, 5, fresh, stale)
+    ref = torch.full((3, 6, 5), -1.0, dtype=torch.bfloat16)
+    ref[:, 2:4] = fresh.cpu().view(3, 2, 5)
+    assert torch.equal(stale.cpu().view(3, 6, 5), ref)
+
+
+def test_stale_equals_fresh_matches_oracle():
+    wl = W["sdxl1024_l3"].with_patch(2)
+    d = cpu_inputs(wl, stale_equals_fresh=True)
+    g = gpu_copy(d)
+    assert_close(to_np(_run_attention(wl, g)), _oracle_attention(wl, d), "bf16", "attention stale=fresh")
+    y = dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], g["x_stale"], g["weight"], g["bias"])
+    ref = oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, d["x_fresh"], d["x_stale"],
+                                    d["weight"], d["bias"])
+    assert_close(to_np(y), ref, "bf16", "conv stale=fresh")
+
+
+def test_nan_poison_of_unread_regions_changes_nothing():
+    wl = RAGGED_BF16.with_patch(2)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    base_attn = _run_attention(wl, g)
+    base_conv = dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], g["x_stale"], g["weight"], g["bias"])
+    base_gn, _ = dp.distri_async_groupnorm(wl.geom, wl.groups, g["x_fresh"], g["table"], g["gamma"],
+                                           g["beta"])
+    lo, hi = 2 * wl.lq, 3 * wl.lq
+    p = dict(g)
+    p["k_stale"] = g["k_stale"].clone()
+    p["v_stale"] = g["v_stale"].clone()
+    p["k_stale"][:, lo:hi] = float("nan")
+    p["v_stale"][:, lo:hi] = float("nan")
+    xs = torch.full_like(g["x_stale"], float("nan"))
+    h = wl.h
+    xs[:, 2 * h - 1] = g["x_stale"][:, 2 * h - 1]
+    xs[:, 3 * h] = g["x_stale"][:, 3 * h]
+    tab = g["table"].clone()
+    tab[:, 2] = float("nan")
+    assert torch.equal(_run_attention(wl, p), base_attn)
+    assert torch.equal(dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], xs, g["weight"], g["bias"]),
+                       base_conv)
+    assert torch.equal(dp.distri_async_groupnorm(wl.geom, wl.groups, g["x_fresh"], tab, g["gamma"],
+                                                 g["beta"])[0], base_gn)
+
+
+def test_guard_regions_untouched_and_deterministic():
+    wl = RAGGED_BF16.with_patch(1)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    n_out = g["q"].numel()
+    guard = 4096
+    buf = torch.full((n_out + 2 * guard,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[guard:guard + n_out].view(g["q"].shape)
+    dp.distri_patch_self_attn(wl.geom, wl.heads, g["q"], g["k_fresh"], g["v_fresh"], g["k_stale"],
+                              g["v_stale"], out=out)
+    again = _run_attention(wl, g)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:guard] == 7.0) and torch.all(buf[guard + n_out:] == 7.0)
+    assert torch.equal(out, again)
+    n_y = g["x_fresh"].numel()
+    buf = torch.full((n_y + 2 * guard,), 7.0, dtype=torch.bfloat16, device="cuda")
+    y = buf[guard:guard + n_y].view(g["x_fresh"].shape)
+    dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], g["x_stale"], g["weight"], g["bias"], y=y)
+    assert torch.all(buf[:guard] == 7.0) and torch.all(buf[guard + n_y:] == 7.0)
+    assert torch.equal(y, dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], g["x_stale"], g["weight"],
+                                                       g["bias"]))
+    buf = torch.full((n_y + 2 * guard,), 7.0, dtype=torch.bfloat16, device="cuda")
+    yg = buf[guard:guard + n_y].view(g["x_fresh"].shape)
+    dp.distri_async_groupnorm(wl.geom, wl.groups, g["x_fresh"], g["table"], g["gamma"], g["beta"], y=yg)
+    assert torch.all(buf[:guard] == 7.0) and torch.all(buf[guard + n_y:] == 7.0)
+
+
+def test_single_patch_needs_no_stale_map():
+    wl = si.Workload("one_patch", 2, 64, 8, 8, 1, 1, seed=99)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    y = dp.distri_patch_conv3x3_halo(wl.geom, g["x_fresh"], None, g["weight"], g["bias"])
+    ref = oracle.patch_conv3x3_halo(wl.geom, 64, 64, d["x_fresh"], d["x_stale"], d["weight"], d["bias"])
+    assert_close(to_np(y), ref, "bf16", "conv n=1")
+    out = _run_attention(wl, g)
+    assert_close(to_np(out), _oracle_attention(wl, d), "bf16", "attention n=1")
+
+
+def test_empty_batch_is_a_no_op():
+    geom = (0, 8, 8, 2, 0)
+    e = torch.empty(0, dtype=torch.bfloat16, device="cuda")
+    dp.distri_patch_self_attn(geom, 1, e, e, e, e, e, out=e)
+    dp.distri_refresh_stale(geom, 64, e, e)
+    torch.cuda.synchronize()
+
+
+def test_extreme_scores_stay_finite():
+    """Large-magnitude logits: the online softmax must rescale correctly."""
+    wl = si.Workload("hot", 1, 64, 16, 16, 2, 1, seed=7)
+    d = cpu_inputs(wl)
+    d = dict(d)
+    d["q"] = (d["q"].float() * 6).to(torch.bfloat16)
+    g = gpu_copy(d)
+    out = _run_attention(wl, g)
+    assert_close(to_np(out), _oracle_attention(wl, d), "bf16", "attention large logits")
