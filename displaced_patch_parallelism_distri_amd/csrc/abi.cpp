@@ -81,6 +81,9 @@ int check_attn_shape(const distri_patch_geom* g, int64_t heads, int64_t head_dim
     DP_CHECK(heads <= 65535 / (g->batch > 0 ? g->batch : 1), DISTRI_ERR_UNSUPPORTED,
              "batch * heads above 65535");
     DP_CHECK(head_dim == 64, DISTRI_ERR_UNSUPPORTED, "head_dim must be 64");
+    // the kernels index one image's tokens with 32-bit offsets
+    DP_CHECK(g->height * g->width * heads * head_dim < (int64_t(1) << 31), DISTRI_ERR_UNSUPPORTED,
+             "height * width * heads * head_dim must stay below 2^31");
     return DISTRI_OK;
 }
 
@@ -94,7 +97,7 @@ int check_gn_shape(const distri_patch_geom* g, int64_t C, int64_t G, int dtype) 
     const int vec = 16 / elem_bytes_of(dtype);
     DP_CHECK(C % vec == 0, DISTRI_ERR_UNSUPPORTED,
              "channels must be a multiple of 8 (bf16) or 4 (fp32)");
-    DP_CHECK(C / vec <= 1024, DISTRI_ERR_UNSUPPORTED, "channels above 8192 (bf16) / 4096 (fp32)");
+    DP_CHECK(C / vec <= 512, DISTRI_ERR_UNSUPPORTED, "channels above 4096 (bf16) / 2048 (fp32)");
     return DISTRI_OK;
 }
 

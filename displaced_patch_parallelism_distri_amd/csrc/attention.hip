@@ -12,8 +12,15 @@
 // is loaded.
 //
 // bf16 kernel (gfx950, bf16 MFMA, fp32 accumulation):
-//  * block = 4 waves x 64 queries; every wave keeps its Q^T fragments in
-//    registers for the whole key loop;
+//  * block = 4 waves x 64 queries (a 256-query tile of one image and head);
+//    every wave keeps its Q^T fragments in registers for the whole key loop;
+//  * work plan: with P = 2 blocks per CU running at once, whole (tile, head,
+//    image) tasks are handed out in full rounds of P blocks; the tasks left
+//    over are split along the keys into S chunks (S from a small cost model)
+//    so the last round also fills the machine, and a combine kernel merges
+//    the chunks' partial (O, max, sum).  Block ids are remapped so that the
+//    blocks one XCD runs at the same time hold neighbouring tiles of the same
+//    head and walk the same keys together, sharing K/V tiles in that XCD's L2;
 //  * key tiles of 64 rows are staged in LDS, double-buffered: K row-major
 //    (MFMA A operand for S^T = K Q^T) and V transposed to V^T[d][key] while it
 //    is written (A operand for O^T = V^T P^T), so every MFMA operand is a
@@ -47,6 +54,19 @@ constexpr int QB = 2;        // 32-query blocks per wave
 constexpr int QTILE = NWAVES * QB * 32;
 constexpr int KPITCH = D + 8;   // LDS row pitch of K (bf16 elements)
 constexpr int VPITCH = KT + 4;  // LDS row pitch of V^T (bf16 elements)
+constexpr int kPartialCost = 3; // cost of one partial write + merge, in key tiles
+
+// Work plan shared by the host launcher and both kernels.
+struct Plan {
+    int64_t tasks;  // images * heads * query tiles
+    int nqt, nkt;   // query tiles per (image, head); key tiles
+    int P;          // blocks resident at once (multiple of 8)
+    int64_t F;      // tasks run whole, in full rounds of P blocks
+    int R;          // tasks left over, each split into S key chunks
+    int S;
+    int64_t grid() const { return F + int64_t(R) * S; }
+    int64_t partials() const { return S > 1 ? int64_t(R) * S : 0; }
+};
 
 struct AttnArgs {
     const uint16_t* q;
@@ -55,80 +75,128 @@ struct AttnArgs {
     const uint16_t* ks;
     const uint16_t* vs;
     uint16_t* out;
-    int64_t lq;      // local queries per image
-    int64_t L;       // tokens per image
-    int64_t own_lo;  // first token of the patch
+    float* part_o;   // [partials][D][QTILE]  unnormalised O
+    float* part_ml;  // [partials][QTILE][2]  (running max, sum)
+    int lq;          // local queries per image
+    int L;           // tokens per image
+    int own_lo;      // first token of the patch
     int heads;
     float c;         // scale * log2(e)
+    Plan plan;
 };
 
-__device__ __forceinline__ const uint16_t* token_row(const uint16_t* fresh, const uint16_t* stale,
-                                                     int64_t b, int64_t hd, int64_t t,
-                                                     const AttnArgs& a) {
-    const int64_t rel = t - a.own_lo;
-    if (rel >= 0 && rel < a.lq) return fresh + ((b * a.lq + rel) * a.heads + hd) * D;
-    return stale + ((b * a.L + t) * a.heads + hd) * D;
+Plan make_plan(int64_t B, int64_t heads, int64_t lq, int64_t L, int cus) {
+    Plan p;
+    p.nqt = int(ceil_div(lq, QTILE));
+    p.nkt = int(ceil_div(L, KT));
+    p.tasks = B * heads * p.nqt;
+    p.P = 2 * (cus > 4 ? cus : 4);
+    p.P -= p.P % 8;
+    p.F = (p.tasks / p.P) * p.P;
+    p.R = int(p.tasks - p.F);
+    p.S = 1;
+    if (p.R > 0) {
+        int64_t best = -1;
+        const int smax = p.nkt < 32 ? p.nkt : 32;
+        for (int S = 1; S <= smax; ++S) {
+            const int64_t rounds = ceil_div(int64_t(p.R) * S, p.P);
+            const int64_t cost = rounds * (ceil_div(p.nkt, S) + (S > 1 ? kPartialCost : 0));
+            if (best < 0 || cost < best) {
+                best = cost;
+                p.S = S;
+            }
+        }
+    }
+    return p;
 }
 
-__device__ __forceinline__ uint32_t half_of(const u32x4& v, int e) {
-    const uint32_t w = v[e >> 1];
-    return (e & 1) ? (w >> 16) : (w & 0xffffu);
+// Physical position w of n blocks -> logical index, so that the blocks the
+// hardware places on one XCD (w % 8) get one contiguous logical range.
+__device__ __forceinline__ int xcd_remap(int w, int n) {
+    const int n8 = n - n % 8;
+    if (w >= n8) return w;
+    return (w % 8) * (n8 / 8) + w / 8;
 }
 
 __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VPITCH];
+    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+    const Plan& pl = a.plan;
+
+    // ---- which (task, key range) this block owns
+    const int64_t bid = blockIdx.x;
+    int64_t task, part = -1;
+    int kt0, kt1;
+    if (bid < pl.F) {
+        task = (bid / pl.P) * pl.P + xcd_remap(int(bid % pl.P), pl.P);
+        kt0 = 0;
+        kt1 = pl.nkt;
+    } else {
+        const int i2 = xcd_remap(int(bid - pl.F), pl.R * pl.S);
+        const int c = i2 / pl.R, r = i2 % pl.R;
+        task = pl.F + r;
+        kt0 = int(int64_t(c) * pl.nkt / pl.S);
+        kt1 = int(int64_t(c + 1) * pl.nkt / pl.S);
+        if (pl.S > 1) part = int64_t(r) * pl.S + c;
+    }
+    const int64_t bh = task / pl.nqt;
+    const int qt = int(task % pl.nqt);
+    const int64_t b = bh / a.heads, hd = bh % a.heads;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 31, g = lane >> 5;
-    const int64_t bh = blockIdx.y;
-    const int64_t b = bh / a.heads, hd = bh % a.heads;
-    const int64_t q0 = int64_t(blockIdx.x) * QTILE + wave * (QB * 32);
+    const int q0 = qt * QTILE + wave * (QB * 32);
+    const int rs = a.heads * D;  // elements between consecutive tokens
 
     // Q^T fragments (MFMA B operand): lane holds query q0+qb*32+lr, dims
     // ks*16 + g*8 .. +8.
     bf16x8 qf[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-        int64_t row = q0 + qb * 32 + lr;
+        int row = q0 + qb * 32 + lr;
         if (row > a.lq - 1) row = a.lq - 1;
-        const uint16_t* qp = a.q + ((b * a.lq + row) * a.heads + hd) * D + g * 8;
+        const uint16_t* qp = a.q + (b * a.lq * a.heads + hd) * D + int64_t(row) * rs + g * 8;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
     }
 
-    // tile-load mapping: K rows kk and kk+32, V rows 2u and 2u+1, 8 dims each
+    // tile-load mapping: K rows kk and kk+32, V rows 2kk and 2kk+1, 8 dims each.
+    // A token row comes from the fresh slice inside the patch, else from the
+    // stale map (32-bit offsets: the ABI bounds L * heads * D below 2^31).
     const int c8 = tid & 7;
     const int kk = tid >> 3;
+    const uint16_t* kst = a.ks + (b * a.L * a.heads + hd) * D + c8 * 8;
+    const uint16_t* vst = a.vs + (b * a.L * a.heads + hd) * D + c8 * 8;
+    const uint16_t* kfr = a.kf + (b * a.lq * a.heads + hd) * D + c8 * 8;
+    const uint16_t* vfr = a.vf + (b * a.lq * a.heads + hd) * D + c8 * 8;
+    auto row_ptr = [&](const uint16_t* fr, const uint16_t* st, int t) {
+        const int rel = t - a.own_lo;
+        return unsigned(rel) < unsigned(a.lq) ? fr + rel * rs : st + t * rs;
+    };
     u32x4 kr[2], vr[2];
-    const int64_t ntiles = ceil_div(a.L, KT);
-
-    auto gload = [&](int64_t kt) {
-        const int64_t t0 = kt * KT;
+    auto gload = [&](int kt) {
+        const int t0 = kt * KT;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int64_t t = t0 + kk + 32 * j;
-            if (t < a.L)
-                kr[j] = *reinterpret_cast<const u32x4*>(token_row(a.kf, a.ks, b, hd, t, a) + c8 * 8);
-            else
-                kr[j] = u32x4{0, 0, 0, 0};
-            const int64_t tv = t0 + 2 * kk + j;
-            if (tv < a.L)
-                vr[j] = *reinterpret_cast<const u32x4*>(token_row(a.vf, a.vs, b, hd, tv, a) + c8 * 8);
-            else
-                vr[j] = u32x4{0, 0, 0, 0};
+            const int t = t0 + kk + 32 * j;
+            kr[j] = t < a.L ? *reinterpret_cast<const u32x4*>(row_ptr(kfr, kst, t)) : u32x4{0, 0, 0, 0};
+            const int tv = t0 + 2 * kk + j;
+            vr[j] = tv < a.L ? *reinterpret_cast<const u32x4*>(row_ptr(vfr, vst, tv)) : u32x4{0, 0, 0, 0};
         }
     };
     auto lstore = [&](int buf) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             *reinterpret_cast<u32x4*>(&k_lds[buf][(kk + 32 * j) * KPITCH + c8 * 8]) = kr[j];
+        // V^T[d][key]: pack (V[2kk][d], V[2kk+1][d]) into one dword per d
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t w = half_of(vr[0], e) | (half_of(vr[1], e) << 16);
-            *reinterpret_cast<uint32_t*>(&v_lds[buf][(c8 * 8 + e) * VPITCH + 2 * kk]) = w;
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = __builtin_amdgcn_perm(vr[1][j], vr[0][j], 0x05040100u);
+            const uint32_t hi = __builtin_amdgcn_perm(vr[1][j], vr[0][j], 0x07060302u);
+            *reinterpret_cast<uint32_t*>(&v_lds[buf][(c8 * 8 + 2 * j) * VPITCH + 2 * kk]) = lo;
+            *reinterpret_cast<uint32_t*>(&v_lds[buf][(c8 * 8 + 2 * j + 1) * VPITCH + 2 * kk]) = hi;
         }
     };
 
@@ -144,20 +212,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         l[qb] = 0.f;
     }
 
-    gload(0);
+    gload(kt0);
     lstore(0);
     __syncthreads();
 
-    for (int64_t kt = 0; kt < ntiles; ++kt) {
-        const int cur = int(kt & 1);
-        if (kt + 1 < ntiles) gload(kt + 1);
+    for (int kt = kt0; kt < kt1; ++kt) {
+        const int cur = (kt - kt0) & 1;
+        if (kt + 1 < kt1) gload(kt + 1);
 
         // S^T = K Q^T : s[kb][qb] covers keys kb*32.. and queries qb*32..
         f32x16 s[2][QB];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int qb = 0; qb < QB; ++qb) s[kb][qb] = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -166,8 +230,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                     &k_lds[cur][(kb * 32 + lr) * KPITCH + ks * 16 + g * 8]);
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[qb][ks], s[kb][qb],
-                                                                        0, 0, 0);
+                    s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        ka, qf[qb][ks], ks == 0 ? f32x16{} : s[kb][qb], 0, 0, 0);
             }
         }
         // keys past the end of the map (last tile only)
@@ -176,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
-                    const int64_t key = kt * KT + kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+                    const int key = kt * KT + kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
                     if (key >= a.L)
 #pragma unroll
                         for (int qb = 0; qb < QB; ++qb) s[kb][qb][j] = -INFINITY;
@@ -203,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 m[qb] = mnew;
             }
             const float mneg = -m[qb];
-            float rs = 0.f;
+            float rsum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -217,10 +281,10 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                     // multiplies, so the normalisation matches the numerator
 #pragma unroll
                     for (int e = 0; e < 8; e += 2)
-                        rs = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, kOnes, rs, false);
+                        rsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, kOnes, rsum, false);
                 }
             }
-            l[qb] += rs;
+            l[qb] += rsum;
         }
 
         // O^T += V^T P^T.  B operand slot e of k-step (kb, h2) holds key
@@ -245,29 +309,98 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             }
         }
 
-        if (kt + 1 < ntiles) lstore(cur ^ 1);
+        if (kt + 1 < kt1) lstore(cur ^ 1);
         __syncthreads();
     }
 
-    // epilogue: O = O^T / l, lane writes 4-dim runs of its query row
+    if (part < 0) {
+        // whole task: O = O^T / l, lane writes 4-dim runs of its query row
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) {
-        const float ltot = l[qb] + __shfl_xor(l[qb], 32);
-        const float inv = 1.0f / ltot;
-        const int64_t row = q0 + qb * 32 + lr;
-        if (row < a.lq) {
-            uint16_t* op = a.out + ((b * a.lq + row) * a.heads + hd) * D;
+        for (int qb = 0; qb < QB; ++qb) {
+            const float inv = 1.0f / (l[qb] + __shfl_xor(l[qb], 32));
+            const int row = q0 + qb * 32 + lr;
+            if (row < a.lq) {
+                uint16_t* op = a.out + (b * a.lq * a.heads + hd) * D + int64_t(row) * rs;
+#pragma unroll
+                for (int db = 0; db < 2; ++db)
+#pragma unroll
+                    for (int jg = 0; jg < 4; ++jg) {
+                        u32x2 w;
+                        w[0] = pack_bf16x2(o[db][qb][4 * jg] * inv, o[db][qb][4 * jg + 1] * inv);
+                        w[1] = pack_bf16x2(o[db][qb][4 * jg + 2] * inv, o[db][qb][4 * jg + 3] * inv);
+                        *reinterpret_cast<u32x2*>(op + db * 32 + 8 * jg + 4 * g) = w;
+                    }
+            }
+        }
+    } else {
+        // one key chunk of a split task: unnormalised O^T, max and sum
+        float* po = a.part_o + part * D * QTILE;
+        float* pml = a.part_ml + part * QTILE * 2;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+            const float ltot = l[qb] + __shfl_xor(l[qb], 32);
+            const int row = wave * (QB * 32) + qb * 32 + lr;
 #pragma unroll
             for (int db = 0; db < 2; ++db)
 #pragma unroll
-                for (int jg = 0; jg < 4; ++jg) {
-                    u32x2 w;
-                    w[0] = pack_bf16x2(o[db][qb][4 * jg] * inv, o[db][qb][4 * jg + 1] * inv);
-                    w[1] = pack_bf16x2(o[db][qb][4 * jg + 2] * inv, o[db][qb][4 * jg + 3] * inv);
-                    *reinterpret_cast<u32x2*>(op + db * 32 + 8 * jg + 4 * g) = w;
-                }
+                for (int j = 0; j < 16; ++j)
+                    po[(db * 32 + 8 * (j >> 2) + 4 * g + (j & 3)) * QTILE + row] = o[db][qb][j];
+            if (g == 0) {
+                pml[row * 2 + 0] = m[qb];
+                pml[row * 2 + 1] = ltot;
+            }
         }
     }
+}
+
+// Merge the S key chunks of each split task: one thread per query row.
+__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+    const Plan& pl = a.plan;
+    const int r = blockIdx.x;
+    const int64_t task = pl.F + r;
+    const int64_t bh = task / pl.nqt;
+    const int qt = int(task % pl.nqt);
+    const int64_t b = bh / a.heads, hd = bh % a.heads;
+    const int row = threadIdx.x;
+    const int qrow = qt * QTILE + row;
+    if (qrow >= a.lq) return;
+    const int64_t p0 = int64_t(r) * pl.S;
+    float M = -INFINITY;
+    for (int c = 0; c < pl.S; ++c) M = fmaxf(M, a.part_ml[((p0 + c) * QTILE + row) * 2]);
+    float acc[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    float lsum = 0.f;
+    for (int c = 0; c < pl.S; ++c) {
+        const float* ml = a.part_ml + ((p0 + c) * QTILE + row) * 2;
+        const float w = __builtin_amdgcn_exp2f(ml[0] - M);
+        lsum = fmaf(w, ml[1], lsum);
+        const float* po = a.part_o + (p0 + c) * D * QTILE + row;
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(w, po[d * QTILE], acc[d]);
+    }
+    const float inv = 1.0f / lsum;
+    uint16_t* op = a.out + (b * a.lq * a.heads + hd) * D + int64_t(qrow) * a.heads * D;
+#pragma unroll
+    for (int d8 = 0; d8 < D / 8; ++d8) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            w[j] = pack_bf16x2(acc[d8 * 8 + 2 * j] * inv, acc[d8 * 8 + 2 * j + 1] * inv);
+        *reinterpret_cast<u32x4*>(op + d8 * 8) = w;
+    }
+}
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+    if (dev < 64) cached[dev] = cus;
+    return cus;
 }
 
 // ----------------------------------------------------------------- fp32 path
@@ -346,13 +479,21 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgsF32 a) {
 
 }  // namespace
 
-size_t attention_workspace_bytes(const Geom&, int64_t, bool) { return 0; }
+size_t attention_workspace_bytes(const Geom& g, int64_t heads, bool bf16) {
+    if (!bf16) return 0;
+    const int cus = device_cus();
+    if (cus <= 0) return 0;
+    const Plan p = make_plan(g.B, heads, g.lq(), g.L(), cus);
+    return size_t(p.partials()) * QTILE * (D + 2) * sizeof(float);
+}
 
 hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16, const void* q,
                             const void* kf, const void* vf, const void* ks, const void* vs,
-                            void* out, void*, hipStream_t s) {
+                            void* out, void* ws, hipStream_t s) {
     const int64_t lq = g.lq();
     if (bf16) {
+        const int cus = device_cus();
+        if (cus <= 0) return hipErrorNoDevice;
         AttnArgs a;
         a.q = static_cast<const uint16_t*>(q);
         a.kf = static_cast<const uint16_t*>(kf);
@@ -360,13 +501,18 @@ hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16
         a.ks = static_cast<const uint16_t*>(ks);
         a.vs = static_cast<const uint16_t*>(vs);
         a.out = static_cast<uint16_t*>(out);
-        a.lq = lq;
-        a.L = g.L();
-        a.own_lo = g.i * lq;
+        a.plan = make_plan(g.B, heads, lq, g.L(), cus);
+        a.part_o = static_cast<float*>(ws);
+        a.part_ml = a.part_o + a.plan.partials() * D * QTILE;
+        a.lq = int(lq);
+        a.L = int(g.L());
+        a.own_lo = int(g.i * lq);
         a.heads = int(heads);
         a.c = scale * 1.4426950408889634f;
-        dim3 grid(unsigned(ceil_div(lq, QTILE)), unsigned(g.B * heads));
-        hipLaunchKernelGGL(attn_bf16_kernel, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_bf16_kernel, dim3(unsigned(a.plan.grid())), dim3(256), 0, s, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.plan.partials() == 0) return e;
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(a.plan.R)), dim3(QTILE), 0, s, a);
         return hipGetLastError();
     }
     AttnArgsF32 a;

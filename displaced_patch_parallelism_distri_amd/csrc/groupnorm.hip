@@ -16,8 +16,8 @@
 //                     pixels contiguously.  Per-channel fp32 partials are
 //                     folded into per-group partials in LDS and written to
 //                     the workspace [B][chunks][G][2].
-//   2. gn_finalize  - per image: fp64 sum of the chunk partials in a fixed
-//                     order, the fresh/stale mix, the clamp, and the
+//   2. gn_finalize  - per (group, image): fp64 sum of the chunk partials in a
+//                     fixed order, the fresh/stale mix, the clamp, and the
 //                     per-channel affine (a_c = rstd gamma_c,
 //                     b_c = beta_c - mu a_c) written to the workspace.
 //   3. gn_normalize - second coalesced pass: y = x a_c + b_c, rounded (RNE).
@@ -27,7 +27,8 @@
 namespace dp {
 namespace {
 
-constexpr int kTargetBlocks = 1024;
+constexpr int kTargetBlocks = 512;
+constexpr int kUnroll = 4;
 
 struct GnPlan {
     int vpp;        // 16-byte vectors per pixel
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(1024) void gn_moments(const typename T::elem* __res
                                                    int64_t P, int C, int vpp, int rows, int G,
                                                    int64_t ppc, int64_t chunks,
                                                    float* __restrict__ partial) {
-    extern __shared__ float lds[];  // [2][rows][C]
+    extern __shared__ float lds[];  // [2][rows][C], then [2][C] channel totals
     const int64_t b = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x;
     const int col = tid % vpp, row = tid / vpp;
@@ -77,13 +78,23 @@ __global__ __launch_bounds__(1024) void gn_moments(const typename T::elem* __res
 #pragma unroll
     for (int j = 0; j < T::VEC; ++j) s[j] = ss[j] = 0.f;
     const u32x4* base = reinterpret_cast<const u32x4*>(x + b * P * C) + col;
-    for (int64_t p = p0 + row; p < p1; p += rows) {
-        float v[T::VEC];
-        T::unpack(base[p * vpp], v);
+    // kUnroll independent 16-byte loads in flight per thread
+    for (int64_t p = p0 + row; p < p1; p += int64_t(kUnroll) * rows) {
+        u32x4 v[kUnroll];
 #pragma unroll
-        for (int j = 0; j < T::VEC; ++j) {
-            s[j] += v[j];
-            ss[j] = fmaf(v[j], v[j], ss[j]);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t pu = p + int64_t(u) * rows;
+            v[u] = pu < p1 ? base[pu * vpp] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            float f[T::VEC];
+            T::unpack(v[u], f);
+#pragma unroll
+            for (int j = 0; j < T::VEC; ++j) {
+                s[j] += f[j];
+                ss[j] = fmaf(f[j], f[j], ss[j]);
+            }
         }
     }
 #pragma unroll
@@ -92,17 +103,27 @@ __global__ __launch_bounds__(1024) void gn_moments(const typename T::elem* __res
         lds[rows * C + row * C + col * T::VEC + j] = ss[j];
     }
     __syncthreads();
+    // channel totals over the block's rows (fixed order)
+    float* tot = lds + 2 * rows * C;
+    for (int t = tid; t < 2 * C; t += blockDim.x) {
+        const int stat = t / C, c = t % C;
+        float acc = 0.f;
+        for (int r = 0; r < rows; ++r) acc += lds[stat * rows * C + r * C + c];
+        tot[stat * C + c] = acc;
+    }
+    __syncthreads();
     const int cg = C / G;
     for (int task = tid; task < 2 * G; task += blockDim.x) {
         const int g = task >> 1, stat = task & 1;
-        const float* src = lds + stat * rows * C + g * cg;
+        const float* src = tot + stat * C + g * cg;
         float acc = 0.f;
-        for (int r = 0; r < rows; ++r)
-            for (int c = 0; c < cg; ++c) acc += src[r * C + c];
+        for (int c = 0; c < cg; ++c) acc += src[c];
         partial[((b * chunks + chunk) * G + g) * 2 + stat] = acc;
     }
 }
 
+// One block per (group, image): fixed-order fp64 reduction of the chunk
+// partials, the fresh/stale mix and the clamp, then the per-channel affine.
 __global__ __launch_bounds__(256) void gn_finalize(const float* __restrict__ partial,
                                                    int64_t chunks, int C, int G, int64_t n,
                                                    int64_t patch, double count, float eps,
@@ -111,16 +132,29 @@ __global__ __launch_bounds__(256) void gn_finalize(const float* __restrict__ par
                                                    const float* __restrict__ beta,
                                                    float* __restrict__ fresh_moments,
                                                    float* __restrict__ affine) {
-    const int64_t b = blockIdx.x;
-    const int cg = C / G;
-    for (int g = threadIdx.x; g < G; g += blockDim.x) {
-        double s1 = 0.0, s2 = 0.0;
-        const float* pp = partial + (b * chunks * G + g) * 2;
-        for (int64_t k = 0; k < chunks; ++k) {
-            s1 += double(pp[k * G * 2 + 0]);
-            s2 += double(pp[k * G * 2 + 1]);
+    __shared__ double red[2][256];
+    __shared__ double stats[2];
+    const int g = blockIdx.x;
+    const int64_t b = blockIdx.y;
+    const int tid = threadIdx.x;
+    double s1 = 0.0, s2 = 0.0;
+    const float* pp = partial + (b * chunks * G + g) * 2;
+    for (int64_t k = tid; k < chunks; k += 256) {
+        s1 += double(pp[k * G * 2 + 0]);
+        s2 += double(pp[k * G * 2 + 1]);
+    }
+    red[0][tid] = s1;
+    red[1][tid] = s2;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (tid < w) {
+            red[0][tid] += red[0][tid + w];
+            red[1][tid] += red[1][tid + w];
         }
-        const double m1 = s1 / count, m2 = s2 / count;
+        __syncthreads();
+    }
+    if (tid == 0) {
+        const double m1 = red[0][0] / count, m2 = red[1][0] / count;
         fresh_moments[(b * G + g) * 2 + 0] = float(m1);
         fresh_moments[(b * G + g) * 2 + 1] = float(m2);
         double e1 = m1, e2 = m2;
@@ -133,14 +167,18 @@ __global__ __launch_bounds__(256) void gn_finalize(const float* __restrict__ par
         e2 /= double(n);
         double var = e2 - e1 * e1;
         if (var < 0.0) var = 0.0;
-        const double rstd = 1.0 / sqrt(var + double(eps));
-        for (int c = g * cg; c < (g + 1) * cg; ++c) {
-            const double ga = gamma ? double(gamma[c]) : 1.0;
-            const double be = beta ? double(beta[c]) : 0.0;
-            const double a = rstd * ga;
-            affine[(b * C + c) * 2 + 0] = float(a);
-            affine[(b * C + c) * 2 + 1] = float(be - e1 * a);
-        }
+        stats[0] = e1;
+        stats[1] = 1.0 / sqrt(var + double(eps));
+    }
+    __syncthreads();
+    const int cg = C / G;
+    const double mu = stats[0], rstd = stats[1];
+    for (int c = g * cg + tid; c < (g + 1) * cg; c += 256) {
+        const double ga = gamma ? double(gamma[c]) : 1.0;
+        const double be = beta ? double(beta[c]) : 0.0;
+        const double a = rstd * ga;
+        affine[(b * C + c) * 2 + 0] = float(a);
+        affine[(b * C + c) * 2 + 1] = float(be - mu * a);
     }
 }
 
@@ -163,12 +201,24 @@ __global__ __launch_bounds__(1024) void gn_normalize(const typename T::elem* __r
     const int64_t p1 = p0 + ppc < P ? p0 + ppc : P;
     const u32x4* src = reinterpret_cast<const u32x4*>(x + b * P * C) + col;
     u32x4* dst = reinterpret_cast<u32x4*>(y + b * P * C) + col;
-    for (int64_t p = p0 + row; p < p1; p += rows) {
-        float v[T::VEC];
-        T::unpack(src[p * vpp], v);
+    for (int64_t p = p0 + row; p < p1; p += int64_t(kUnroll) * rows) {
+        u32x4 v[kUnroll];
 #pragma unroll
-        for (int j = 0; j < T::VEC; ++j) v[j] = fmaf(v[j], a[j], c0[j]);
-        dst[p * vpp] = T::pack(v);
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t pu = p + int64_t(u) * rows;
+            if (pu < p1) v[u] = src[pu * vpp];
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int64_t pu = p + int64_t(u) * rows;
+            if (pu < p1) {
+                float f[T::VEC];
+                T::unpack(v[u], f);
+#pragma unroll
+                for (int j = 0; j < T::VEC; ++j) f[j] = fmaf(f[j], a[j], c0[j]);
+                dst[pu * vpp] = T::pack(f);
+            }
+        }
     }
 }
 
@@ -180,14 +230,14 @@ hipError_t run(const Geom& g, int64_t C, int64_t G, float eps, const void* x,
     const int64_t P = g.h() * g.W;
     float* partial = static_cast<float*>(ws);
     float* affine = partial + g.B * p.chunks * G * 2;
-    const size_t lds = size_t(2) * p.rows * C * sizeof(float);
+    const size_t lds = size_t(2) * (p.rows + 1) * C * sizeof(float);
     dim3 grid(unsigned(p.chunks), unsigned(g.B));
     hipLaunchKernelGGL(gn_moments<T>, grid, dim3(p.threads), lds, s,
                        static_cast<const typename T::elem*>(x), P, int(C), p.vpp, p.rows, int(G),
                        p.ppc, p.chunks, partial);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gn_finalize, dim3(unsigned(g.B)), dim3(256), 0, s, partial, p.chunks,
+    hipLaunchKernelGGL(gn_finalize, dim3(unsigned(G), unsigned(g.B)), dim3(256), 0, s, partial, p.chunks,
                        int(C), int(G), g.n, g.i, double(P) * double(C / G), eps, stale_moments,
                        gamma, beta, fresh_moments, affine);
     e = hipGetLastError();

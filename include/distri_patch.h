@@ -88,11 +88,14 @@ const char *distri_last_error(void);
  *
  *   q, k_fresh, v_fresh, out   [B, Lq, heads, head_dim]   dtype
  *   k_stale, v_stale           [B, L,  heads, head_dim]   dtype
- *   scale                      finite (1/sqrt(head_dim) for SDXL)
+ *   scale                      finite and > 0 (1/sqrt(head_dim) for SDXL)
  *   workspace                  >= distri_patch_self_attn_workspace_size()
  *                              bytes of device memory (may be NULL if that
  *                              size is 0); contents on entry are ignored.
- * head_dim must be 64 (DISTRI_ERR_UNSUPPORTED otherwise).  bf16 inputs are
+ * head_dim must be 64 and H*W*heads*head_dim below 2^31
+ * (DISTRI_ERR_UNSUPPORTED otherwise).  The bf16 path may split the keys of
+ * some query tiles into chunks; the workspace then holds their partial
+ * results (its size depends on the current device's compute-unit count).  bf16 inputs are
  * computed with bf16 MFMA and fp32 accumulation / softmax; fp32 inputs in
  * fp32 throughout.
  */
@@ -144,7 +147,8 @@ int distri_patch_conv3x3_halo(const distri_patch_geom *g, int64_t c_in, int64_t 
  *   fresh_moments   [B, G, 2]     fp32 (output)
  *   workspace       >= distri_async_groupnorm_workspace_size() bytes;
  *                   contents on entry are ignored
- * C must be a multiple of 8 for bf16 and of 4 for fp32 (UNSUPPORTED).
+ * C must be a multiple of 8 for bf16 and of 4 for fp32, and at most 4096
+ * (bf16) / 2048 (fp32) (DISTRI_ERR_UNSUPPORTED).
  */
 int distri_async_groupnorm_workspace_size(const distri_patch_geom *g, int64_t channels,
                                           int64_t groups, int dtype, size_t *bytes);
