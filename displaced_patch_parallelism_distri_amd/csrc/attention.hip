@@ -44,6 +44,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace dp {
 namespace {
 
@@ -165,25 +167,49 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // tile-load mapping: K rows kk and kk+32, V rows 2kk and 2kk+1, 8 dims each.
     // A token row comes from the fresh slice inside the patch, else from the
     // stale map (32-bit offsets: the ABI bounds L * heads * D below 2^31).
+    // Tiles wholly on one side of the patch boundary (all but at most two)
+    // take one wave-uniform base pointer; a straddling tile selects per row.
     const int c8 = tid & 7;
     const int kk = tid >> 3;
-    const uint16_t* kst = a.ks + (b * a.L * a.heads + hd) * D + c8 * 8;
-    const uint16_t* vst = a.vs + (b * a.L * a.heads + hd) * D + c8 * 8;
-    const uint16_t* kfr = a.kf + (b * a.lq * a.heads + hd) * D + c8 * 8;
-    const uint16_t* vfr = a.vf + (b * a.lq * a.heads + hd) * D + c8 * 8;
-    auto row_ptr = [&](const uint16_t* fr, const uint16_t* st, int t) {
-        const int rel = t - a.own_lo;
-        return unsigned(rel) < unsigned(a.lq) ? fr + rel * rs : st + t * rs;
-    };
+    const uint16_t* kst = a.ks + (b * a.L * a.heads + hd) * D;
+    const uint16_t* vst = a.vs + (b * a.L * a.heads + hd) * D;
+    const uint16_t* kfr = a.kf + (b * a.lq * a.heads + hd) * D;
+    const uint16_t* vfr = a.vf + (b * a.lq * a.heads + hd) * D;
+    const int roff[4] = {kk * rs + c8 * 8, (kk + 32) * rs + c8 * 8, 2 * kk * rs + c8 * 8,
+                         (2 * kk + 1) * rs + c8 * 8};
+    const int rkey[4] = {kk, kk + 32, 2 * kk, 2 * kk + 1};
     u32x4 kr[2], vr[2];
     auto gload = [&](int kt) {
         const int t0 = kt * KT;
+        const int own_hi = a.own_lo + a.lq;
+        if (t0 + KT <= a.L && (t0 + KT <= a.own_lo || t0 >= own_hi)) {
+            const uint16_t* kb0 = kst + t0 * rs;
+            const uint16_t* vb0 = vst + t0 * rs;
+            kr[0] = *reinterpret_cast<const u32x4*>(kb0 + roff[0]);
+            kr[1] = *reinterpret_cast<const u32x4*>(kb0 + roff[1]);
+            vr[0] = *reinterpret_cast<const u32x4*>(vb0 + roff[2]);
+            vr[1] = *reinterpret_cast<const u32x4*>(vb0 + roff[3]);
+        } else if (t0 >= a.own_lo && t0 + KT <= own_hi) {
+            const uint16_t* kb0 = kfr + (t0 - a.own_lo) * rs;
+            const uint16_t* vb0 = vfr + (t0 - a.own_lo) * rs;
+            kr[0] = *reinterpret_cast<const u32x4*>(kb0 + roff[0]);
+            kr[1] = *reinterpret_cast<const u32x4*>(kb0 + roff[1]);
+            vr[0] = *reinterpret_cast<const u32x4*>(vb0 + roff[2]);
+            vr[1] = *reinterpret_cast<const u32x4*>(vb0 + roff[3]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int t = t0 + kk + 32 * j;
-            kr[j] = t < a.L ? *reinterpret_cast<const u32x4*>(row_ptr(kfr, kst, t)) : u32x4{0, 0, 0, 0};
-            const int tv = t0 + 2 * kk + j;
-            vr[j] = tv < a.L ? *reinterpret_cast<const u32x4*>(row_ptr(vfr, vst, tv)) : u32x4{0, 0, 0, 0};
+            for (int j = 0; j < 4; ++j) {
+                const int t = t0 + rkey[j];
+                const int rel = t - a.own_lo;
+                const bool fresh = unsigned(rel) < unsigned(a.lq);
+                const uint16_t* base = j < 2 ? (fresh ? kfr : kst) : (fresh ? vfr : vst);
+                const int off = (fresh ? rel : t) * rs + c8 * 8;
+                const u32x4 v = t < a.L ? *reinterpret_cast<const u32x4*>(base + off) : u32x4{0, 0, 0, 0};
+                if (j < 2)
+                    kr[j] = v;
+                else
+                    vr[j - 2] = v;
+            }
         }
     };
     auto lstore = [&](int buf) {
@@ -212,11 +238,11 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         l[qb] = 0.f;
     }
 
-    gload(kt0);
-    lstore(0);
-    __syncthreads();
-
-    for (int kt = kt0; kt < kt1; ++kt) {
+    // one key tile: prefetch the next tile into registers, S^T on MFMA,
+    // online softmax, PV on MFMA, then stage the prefetched tile in LDS.
+    // kMask (a std::integral_constant) masks keys past the end of the map;
+    // only the map's last, partial tile needs it.
+    auto tile = [&](int kt, auto kMask) {
         const int cur = (kt - kt0) & 1;
         if (kt + 1 < kt1) gload(kt + 1);
 
@@ -234,8 +260,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                         ka, qf[qb][ks], ks == 0 ? f32x16{} : s[kb][qb], 0, 0, 0);
             }
         }
-        // keys past the end of the map (last tile only)
-        if ((kt + 1) * KT > a.L) {
+        if (decltype(kMask)::value) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -254,9 +279,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) mx = fmaxf(mx, s[kb][qb][j]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float mnew = fmaxf(m[qb], mx * a.c);
+                for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, s[kb][qb][j]);
+            // the other half-wave holds the other 16 keys of each 32-key block
+            // the other half-wave holds the other 16 keys of each 32-key block
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                             false, false);
+            mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            const float mnew = __builtin_fmaxf(m[qb], mx * a.c);
             // exact running max; the rescale is skipped when no row of the
             // wave saw a larger score (wave-uniform branch)
             if (__any(mnew > m[qb])) {
@@ -272,16 +301,22 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
-                    bf16x8 v;
+                    uint32_t w[4];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        v[e] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + e], a.c, mneg));
-                    p[kb][qb][h2] = v;
+                    for (int e = 0; e < 4; ++e)
+                        w[e] = pack_bf16x2(
+                            __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.c, mneg)),
+                            __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.c, mneg)));
                     // the row sum adds the bf16-rounded p that the PV MFMA
-                    // multiplies, so the normalisation matches the numerator
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2)
-                        rsum = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{v[e], v[e + 1]}, kOnes, rsum, false);
+                    // multiplies, so the normalisation matches the numerator.
+                    // (Scalar words on purpose: passing vector elements w[e]
+                    // straight to the builtin made hipcc read w[0] four times.)
+                    const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+                    rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rsum, false);
+                    rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rsum, false);
+                    rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rsum, false);
+                    rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rsum, false);
+                    p[kb][qb][h2] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
                 }
             }
             l[qb] += rsum;
@@ -311,7 +346,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 
         if (kt + 1 < kt1) lstore(cur ^ 1);
         __syncthreads();
-    }
+    };
+
+    gload(kt0);
+    lstore(0);
+    __syncthreads();
+    const int full_end = (kt1 == pl.nkt && a.L % KT != 0) ? kt1 - 1 : kt1;
+    for (int kt = kt0; kt < full_end; ++kt) tile(kt, std::false_type{});
+    if (full_end < kt1) tile(full_end, std::true_type{});
 
     if (part < 0) {
         // whole task: O = O^T / l, lane writes 4-dim runs of its query row
