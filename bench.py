@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-op", choices=["attn", "conv", "gn", "refresh", "copy"],
+                    help="run only this op (--steps times) for counter collection, print nothing else")
+    ap.add_argument("--level", default="sdxl3840_l2", choices=list(LEVELS))
     return ap.parse_args()
 
 
@@ -181,38 +184,83 @@ def per_op(levels, iters):
 
 
 def cpu_baseline(budget_s):
-    """The CPU oracle on a bounded sample of level (a): a few query rows of
-    attention (all images and heads, all 57600 keys) and one output row of the
-    conv; the rate is (sample FLOPs) / (oracle wall time)."""
+    """The CPU oracle on a bounded sample of level (a): the first local query
+    rows of attention (both images, all 10 heads, all 57600 keys) and the
+    first output row of the conv.  Inputs are widened to float64 before the
+    clock starts; the rate is (sample FLOPs) / (oracle wall time)."""
+    import numpy as np
+
     import oracle
     import synthetic_inputs as si
-    import torch
 
     wl = si.WORKLOADS["sdxl3840_l2"].with_patch(4)
     d = si.make_inputs(wl, device="cpu", nonzero_bias=True)
+    f64 = {k: np.ascontiguousarray(v.double().numpy()) for k, v in d.items()}
+    del d
     scale = wl.head_dim ** -0.5
-    # calibrate on 1 row, then scale to the budget
+    args = (f64["q"], f64["k_fresh"], f64["v_fresh"], f64["k_stale"], f64["v_stale"])
     t0 = time.perf_counter()
-    oracle.patch_self_attn(wl.geom, wl.heads, 64, scale, d["q"], d["k_fresh"], d["v_fresh"],
-                           d["k_stale"], d["v_stale"], rows=(0, 1))
-    t1 = time.perf_counter() - t0
-    rows = max(1, min(wl.lq, int(0.8 * budget_s / max(t1, 1e-3))))
+    oracle.patch_self_attn(wl.geom, wl.heads, 64, scale, *args, rows=(0, 16))
+    per_row = (time.perf_counter() - t0) / 16
+    rows = int(max(16, min(wl.lq, 0.85 * budget_s / max(per_row, 1e-6))))
     t0 = time.perf_counter()
-    oracle.patch_self_attn(wl.geom, wl.heads, 64, scale, d["q"], d["k_fresh"], d["v_fresh"],
-                           d["k_stale"], d["v_stale"], rows=(0, rows))
+    oracle.patch_self_attn(wl.geom, wl.heads, 64, scale, *args, rows=(0, rows))
     ta = time.perf_counter() - t0
     t0 = time.perf_counter()
-    oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, d["x_fresh"], d["x_stale"],
-                              d["weight"], d["bias"], rows=(0, 1))
+    oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, f64["x_fresh"], f64["x_stale"],
+                              f64["weight"], f64["bias"], rows=(0, 1))
     tc = time.perf_counter() - t0
     fa = 4.0 * wl.batch * wl.heads * rows * wl.tokens * wl.head_dim
     fc = 2.0 * wl.batch * wl.width * wl.channels * wl.channels * 9
     return {"value": (fa + fc) / (ta + tc) / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": f"sdxl3840 level (a) patch 4: attention for {rows} local query rows x 2 images "
-                      f"x 10 heads over 57600 keys + conv for 1 output row (2 x 240 px x 640 ch), fp64; "
-                      f"{ta + tc:.1f} s",
-            "seconds": ta + tc}
+            "sample": f"sdxl3840 level (a) patch 4, fp64: attention for {rows} local query rows x 2 "
+                      f"images x 10 heads over 57600 keys + conv for 1 output row (2 x 240 px x "
+                      f"640 -> 640 ch); {ta + tc:.1f} s of oracle time",
+            "seconds": round(ta + tc, 2)}
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sdxl3840_l2_traffic.md")
+ATTN_SRC = os.path.join(ROOT, "displaced_patch_parallelism_distri_amd", "csrc", "attention.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the level-(a) attention kernel from the
+    committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None when the
+    kernel source changed since those counters were taken."""
+    import hashlib
+
+    try:
+        text = open(TRAFFIC_FILE).read()
+        src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if ":" in line and line.strip().startswith(("source_sha256", "traffic_bytes_per_launch")):
+            k, v = line.split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != src or "traffic_bytes_per_launch" not in vals:
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
+def profile_op(args):
+    """Run one op --steps times (for rocprofv3 counter runs)."""
+    import torch
+
+    lv = Level(args.level, args.patch, torch.device("cuda:0"))
+    if args.profile_op == "copy":
+        # plain device copy of known size, to calibrate FETCH_SIZE/WRITE_SIZE
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        fn = lambda: dst.copy_(src)
+    else:
+        fn = {"attn": lv.attention, "conv": lv.conv, "gn": lv.groupnorm, "refresh": lv.refresh}[args.profile_op]
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        fn()
+    torch.cuda.synchronize()
 
 
 def main():
@@ -226,6 +274,9 @@ def main():
     import displaced_patch_parallelism_distri_amd as dp
 
     dp.load()
+    if args.profile_op:
+        profile_op(args)
+        return
     dev = torch.device("cuda:0")
     levels = [Level(n, args.patch, dev) for n in LEVELS]
     torch.cuda.synchronize()
@@ -280,7 +331,7 @@ def main():
         "groupnorm_gbps": {k: round(v["groupnorm_gbps"], 1) for k, v in ops.items()},
         "roofline": {"kernel": "attn_bf16_kernel (level a)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "avg_launch_ms": round(attn_ms, 4)},
     }
     if not args.no_cpu_baseline:

@@ -395,10 +395,16 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     }
 }
 
-// Merge the S key chunks of each split task: one thread per query row.
+// Merge the S key chunks of each split task.  Block (task, dim group of 8):
+// one thread per query row; the chunk weights exp2(m_c - M) are recomputed
+// by every dim group (S values), the partial O reads are coalesced across
+// the rows and S * 8 loads per thread stay in flight together.
+constexpr int kCombineDims = 8;
+
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const Plan& pl = a.plan;
     const int r = blockIdx.x;
+    const int d0 = blockIdx.y * kCombineDims;
     const int64_t task = pl.F + r;
     const int64_t bh = task / pl.nqt;
     const int qt = int(task % pl.nqt);
@@ -409,28 +415,24 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int64_t p0 = int64_t(r) * pl.S;
     float M = -INFINITY;
     for (int c = 0; c < pl.S; ++c) M = fmaxf(M, a.part_ml[((p0 + c) * QTILE + row) * 2]);
-    float acc[D];
+    float acc[kCombineDims];
 #pragma unroll
-    for (int d = 0; d < D; ++d) acc[d] = 0.f;
+    for (int d = 0; d < kCombineDims; ++d) acc[d] = 0.f;
     float lsum = 0.f;
     for (int c = 0; c < pl.S; ++c) {
         const float* ml = a.part_ml + ((p0 + c) * QTILE + row) * 2;
         const float w = __builtin_amdgcn_exp2f(ml[0] - M);
         lsum = fmaf(w, ml[1], lsum);
-        const float* po = a.part_o + (p0 + c) * D * QTILE + row;
+        const float* po = a.part_o + ((p0 + c) * D + d0) * QTILE + row;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] = fmaf(w, po[d * QTILE], acc[d]);
+        for (int d = 0; d < kCombineDims; ++d) acc[d] = fmaf(w, po[d * QTILE], acc[d]);
     }
     const float inv = 1.0f / lsum;
-    uint16_t* op = a.out + (b * a.lq * a.heads + hd) * D + int64_t(qrow) * a.heads * D;
+    uint16_t* op = a.out + (b * a.lq * a.heads + hd) * D + int64_t(qrow) * a.heads * D + d0;
+    u32x4 w;
 #pragma unroll
-    for (int d8 = 0; d8 < D / 8; ++d8) {
-        u32x4 w;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            w[j] = pack_bf16x2(acc[d8 * 8 + 2 * j] * inv, acc[d8 * 8 + 2 * j + 1] * inv);
-        *reinterpret_cast<u32x4*>(op + d8 * 8) = w;
-    }
+    for (int j = 0; j < 4; ++j) w[j] = pack_bf16x2(acc[2 * j] * inv, acc[2 * j + 1] * inv);
+    *reinterpret_cast<u32x4*>(op) = w;
 }
 
 int device_cus() {
@@ -554,7 +556,8 @@ hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16
         hipLaunchKernelGGL(attn_bf16_kernel, dim3(unsigned(a.plan.grid())), dim3(256), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.plan.partials() == 0) return e;
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(a.plan.R)), dim3(QTILE), 0, s, a);
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(a.plan.R), D / kCombineDims), dim3(QTILE),
+                           0, s, a);
         return hipGetLastError();
     }
     AttnArgsF32 a;
