@@ -49,6 +49,11 @@ def parse():
     ap.add_argument("--profile-op", choices=["attn", "conv", "gn", "refresh", "copy"],
                     help="run only this op (--steps times) for counter collection, print nothing else")
     ap.add_argument("--level", default="sdxl3840_l2", choices=list(LEVELS))
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown table of a rocprofv3 --kernel-trace run under DIR "
+                         "(library kernels grouped by name and grid) and exit; needs no GPU")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print per-kernel means of every rocprofv3 --pmc run under DIR and exit")
     return ap.parse_args()
 
 
@@ -263,8 +268,60 @@ def profile_op(args):
     torch.cuda.synchronize()
 
 
+def _short_kernel(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return name.split("(")[0].replace("unsigned int __vector", "u32x4")
+
+
+def summarize_trace(d):
+    """Per (kernel, grid) launch count and mean/min/max duration in us, from
+    rocprofv3's kernel trace csv."""
+    import collections
+    import csv
+    import glob
+
+    path = glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True)[0]
+    agg = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if "dp::" not in r["Kernel_Name"]:
+            continue
+        grid = "%sx%sx%s / %s" % (r["Grid_Size_X"], r["Grid_Size_Y"], r["Grid_Size_Z"], r["Workgroup_Size_X"])
+        agg[(_short_kernel(r["Kernel_Name"]), grid, r["VGPR_Count"], r["Accum_VGPR_Count"],
+             r["LDS_Block_Size"])].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | grid (threads) / block | VGPR | AGPR | LDS B | calls | mean us | min us | max us |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for (k, g, v, a, l), t in sorted(agg.items()):
+        print(f"| {k} | {g} | {v} | {a} | {l} | {len(t)} | {sum(t) / len(t):.2f} | {min(t):.2f} | {max(t):.2f} |")
+
+
+def summarize_counters(d):
+    """Per (run, kernel, counter) mean over dispatches, from rocprofv3's
+    counter collection csv files."""
+    import collections
+    import csv
+    import glob
+
+    print("| run | kernel | counter | dispatches | mean |")
+    print("|---|---|---|---|---|")
+    for path in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        run = os.path.relpath(os.path.dirname(path), d)
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            k = _short_kernel(r["Kernel_Name"])
+            if k.startswith("dp::") or "copyBuffer" in k:
+                agg[(k, r["Counter_Name"])].append(float(r["Counter_Value"]))
+        for (k, c), v in sorted(agg.items()):
+            print(f"| {run} | {k} | {c} | {len(v)} | {sum(v) / len(v):.1f} |")
+
+
 def main():
     args = parse()
+    if args.summarize_trace or args.summarize_counters:
+        if args.summarize_trace:
+            summarize_trace(args.summarize_trace)
+        if args.summarize_counters:
+            summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the multi-GPU exchange is a design note, not part of this build)", file=sys.stderr)
@@ -329,7 +386,8 @@ def main():
         "ms_per_layer": {"sdxl3840_l2": round(la[len(la) // 2], 4), "sdxl3840_l3": round(lb[len(lb) // 2], 4)},
         "per_op": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
         "groupnorm_gbps": {k: round(v["groupnorm_gbps"], 1) for k, v in ops.items()},
-        "roofline": {"kernel": "attn_bf16_kernel (level a)", "bound": "mfma",
+        "roofline": {"kernel": "attention at level a (attn_bf16_kernel + attn_combine_kernel)",
+                     "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": measured_traffic(),
                      "avg_launch_ms": round(attn_ms, 4)},
