@@ -136,20 +136,27 @@ class Level:
         self.refresh()
 
 
-def time_op(fn, iters, warmup=3):
+def time_op(fn, iters, warmup=3, reps=1):
+    """Median and minimum per-call time (ms) over `iters` samples; a sample
+    is `reps` back-to-back calls between two events, so for the short
+    memory-bound ops the event overhead is amortised while the gaps between
+    consecutive launches still count."""
     import torch
 
-    for _ in range(warmup):
-        fn(0)
+    for k in range(warmup):
+        fn(k)
     torch.cuda.synchronize()
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(iters)]
-    for k, (a, b) in enumerate(evs):
+    k = 0
+    for a, b in evs:
         a.record()
-        fn(k + 1)
+        for _ in range(reps):
+            k += 1
+            fn(k)
         b.record()
     torch.cuda.synchronize()
-    ts = sorted(a.elapsed_time(b) for a, b in evs)
+    ts = sorted(a.elapsed_time(b) / reps for a, b in evs)
     return ts[len(ts) // 2], ts[0]
 
 
@@ -165,7 +172,7 @@ def per_op(levels, iters):
         nrot = max(2, int(math.ceil(600e6 / (2 * slice_bytes))))
         xs = [torch.randn_like(lv.t["x_fresh"], dtype=torch.float32).to(torch.bfloat16) for _ in range(nrot)]
         ys = [torch.empty_like(lv.t["x_fresh"]) for _ in range(nrot)]
-        gn_med, gn_min = time_op(lambda k: lv.groupnorm(xs[k % nrot], ys[k % nrot]), iters)
+        gn_med, gn_min = time_op(lambda k: lv.groupnorm(xs[k % nrot], ys[k % nrot]), iters, reps=10)
         # refresh of the conv-input map, rotating fresh slices and stale maps
         nrot_r = max(2, int(math.ceil(600e6 / (2 * slice_bytes + slice_bytes))))
         stales = [torch.empty(wl.batch, wl.height, wl.width, wl.channels, dtype=torch.bfloat16,
@@ -174,7 +181,7 @@ def per_op(levels, iters):
         import displaced_patch_parallelism_distri_amd as dp
 
         rf_med, rf_min = time_op(lambda k: dp.distri_refresh_stale(
-            lv.geom, wl.width * wl.channels, xs[k % nrot], stales[k % nr]), iters)
+            lv.geom, wl.width * wl.channels, xs[k % nrot], stales[k % nr]), iters, reps=10)
         del xs, ys, stales
         cv_med, cv_min = time_op(lambda k: lv.conv(), iters)
         at_med, at_min = time_op(lambda k: lv.attention(), iters)
@@ -186,6 +193,27 @@ def per_op(levels, iters):
         }
         torch.cuda.empty_cache()
     return res
+
+
+def copy_peak(iters):
+    """Achievable HBM rate of a large copy (read + write bytes / time): the
+    library's refresh kernel over a whole 512 MiB map (n = 1) and torch's
+    device copy of the same buffers."""
+    import torch
+
+    import displaced_patch_parallelism_distri_amd as dp
+
+    nbytes = 512 << 20
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    rows = 1024
+    geom = (1, rows, 1, 1, 0)
+    rf, _ = time_op(lambda k: dp.distri_refresh_stale(geom, nbytes // 2 // rows, src, dst), iters)
+    tc, _ = time_op(lambda k: dst.copy_(src), iters)
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"refresh_kernel_gbps": round(2 * nbytes / rf / 1e6, 1),
+            "torch_copy_gbps": round(2 * nbytes / tc / 1e6, 1), "bytes_copied": nbytes}
 
 
 def cpu_baseline(budget_s):
@@ -364,6 +392,7 @@ def main():
     flops = sum(lv.wl.attn_flops() + lv.wl.conv_flops() for lv in levels)
     value = flops / (step_ms * 1e-3) / 1e12
     ops = per_op(levels, args.op_iters)
+    copy = copy_peak(args.op_iters)
 
     wa = levels[0].wl
     achieved = wa.attn_flops() / (attn_ms * 1e-3) / 1e12
@@ -386,6 +415,7 @@ def main():
         "ms_per_layer": {"sdxl3840_l2": round(la[len(la) // 2], 4), "sdxl3840_l3": round(lb[len(lb) // 2], 4)},
         "per_op": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
         "groupnorm_gbps": {k: round(v["groupnorm_gbps"], 1) for k, v in ops.items()},
+        "hbm_copy_peak": copy,
         "roofline": {"kernel": "attention at level a (attn_bf16_kernel + attn_combine_kernel)",
                      "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",

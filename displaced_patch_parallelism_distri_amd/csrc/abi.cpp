@@ -98,6 +98,7 @@ int check_gn_shape(const distri_patch_geom* g, int64_t C, int64_t G, int dtype) 
     DP_CHECK(C % vec == 0, DISTRI_ERR_UNSUPPORTED,
              "channels must be a multiple of 8 (bf16) or 4 (fp32)");
     DP_CHECK(C / vec <= 512, DISTRI_ERR_UNSUPPORTED, "channels above 4096 (bf16) / 2048 (fp32)");
+    DP_CHECK(G <= 256, DISTRI_ERR_UNSUPPORTED, "more than 256 groups");
     return DISTRI_OK;
 }
 

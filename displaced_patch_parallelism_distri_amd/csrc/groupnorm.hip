@@ -11,215 +11,313 @@
 // Memory-bound; three launches:
 //   1. gn_moments   - coalesced pass over x [B, h*W, C] (NHWC).  A block is a
 //                     (rows x vectors-per-pixel) grid of threads: thread
-//                     (row, col) owns one 16-byte channel vector of every
-//                     R-th pixel of its chunk, so a row of threads reads whole
-//                     pixels contiguously.  Per-channel fp32 partials are
-//                     folded into per-group partials in LDS and written to
-//                     the workspace [B][chunks][G][2].
-//   2. gn_finalize  - per (group, image): fp64 sum of the chunk partials in a
-//                     fixed order, the fresh/stale mix, the clamp, and the
-//                     per-channel affine (a_c = rstd gamma_c,
-//                     b_c = beta_c - mu a_c) written to the workspace.
+//                     (row, col) owns one 16-byte channel vector of KV pixels
+//                     of its chunk (row, row + rows, ...) and issues all KV
+//                     loads before using any, so the whole slice is in flight
+//                     at once.  Per-channel fp32 sums are folded into
+//                     per-group sums in LDS and written to the workspace
+//                     [B][chunks][G][2].
+//   2. gn_finalize  - one block per image: fixed-order fp64 reduction of the
+//                     chunk sums, the fresh/stale mix, the clamp, and the
+//                     per-channel affine a_c = rstd gamma_c,
+//                     b_c = beta_c - mu a_c (workspace [B][C][2]).  All of its
+//                     global loads are issued before any result is needed.
 //   3. gn_normalize - second coalesced pass: y = x a_c + b_c, rounded (RNE).
-// Deterministic: no atomics; every sum has a fixed order.
+// Deterministic: no atomics, every sum has a fixed order.  The second read of
+// x is normally served from L2 / the Infinity Cache: a chunk is read by the
+// same XCD in both passes and the slice is tens of MB.
 #include "dp_common.h"
+
 
 namespace dp {
 namespace {
 
 constexpr int kTargetBlocks = 512;
-constexpr int kUnroll = 4;
+constexpr int kMaxThreads = 512;
+constexpr int kMaxKV = 16;
 
 struct GnPlan {
     int vpp;        // 16-byte vectors per pixel
-    int rows;       // pixel rows per block iteration
+    int rows;       // pixel rows of a block
     int threads;    // vpp * rows
-    int64_t ppc;    // pixels per chunk
-    int64_t chunks; // chunks per image
+    int kv;         // pixels per thread (power of two)
+    int64_t chunks; // chunks (blocks) per image; a chunk is rows * kv pixels
 };
 
 GnPlan plan_gn(const Geom& g, int64_t C, int elem_bytes) {
     GnPlan p;
-    const int vec = 16 / elem_bytes;
-    p.vpp = int(C / vec);
-    int gcd = 64, a = p.vpp;
-    while (a != 0) {
-        int t = gcd % a;
-        gcd = a;
-        a = t;
-    }
-    p.rows = 64 / gcd;
-    while (p.vpp * p.rows < 256) p.rows *= 2;
-    if (p.vpp * p.rows > 1024) p.rows = 1024 / p.vpp > 0 ? 1024 / p.vpp : 1;
+    p.vpp = int(C / (16 / elem_bytes));
+    p.rows = kMaxThreads / p.vpp > 0 ? kMaxThreads / p.vpp : 1;
     p.threads = p.vpp * p.rows;
     const int64_t P = g.h() * g.W;
-    int64_t per_image = kTargetBlocks / (g.B > 0 ? g.B : 1);
-    if (per_image < 1) per_image = 1;
-    int64_t ppc = ceil_div(P, per_image);
-    ppc = ceil_div(ppc, p.rows) * p.rows;
-    if (ppc < 4 * p.rows) ppc = 4 * p.rows;
-    p.ppc = ppc;
-    p.chunks = ceil_div(P, ppc);
+    const int64_t B = g.B > 0 ? g.B : 1;
+    const int64_t per_image = kTargetBlocks / B > 0 ? kTargetBlocks / B : 1;
+    // pixels per thread: a power of two (the kernels are instantiated per
+    // value), the largest that still gives about kTargetBlocks blocks
+    const int64_t want = ceil_div(ceil_div(P, p.rows), per_image);
+    p.kv = 1;
+    while (p.kv * 2 <= want && p.kv * 2 <= kMaxKV) p.kv *= 2;
+    p.chunks = ceil_div(P, int64_t(p.rows) * p.kv);
     return p;
 }
 
-template <class T>
-__global__ __launch_bounds__(1024) void gn_moments(const typename T::elem* __restrict__ x,
-                                                   int64_t P, int C, int vpp, int rows, int G,
-                                                   int64_t ppc, int64_t chunks,
-                                                   float* __restrict__ partial) {
-    extern __shared__ float lds[];  // [2][rows][C], then [2][C] channel totals
+struct GnWorkspace {
+    float* partial;   // [B][chunks][G][2]
+    float* affine;    // [B][C][2]
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+GnWorkspace carve(void* ws, const Geom& g, const GnPlan& p, int64_t C, int64_t G) {
+    char* base = static_cast<char*>(ws);
+    GnWorkspace w;
+    w.partial = reinterpret_cast<float*>(base);
+    base += align256(size_t(g.B * p.chunks * G * 2) * sizeof(float));
+    w.affine = reinterpret_cast<float*>(base);
+    return w;
+}
+
+size_t workspace_bytes(const Geom& g, const GnPlan& p, int64_t C, int64_t G) {
+    return align256(size_t(g.B * p.chunks * G * 2) * sizeof(float)) +
+           size_t(g.B * C * 2) * sizeof(float);
+}
+
+// Thread (row, col) of chunk `chunk` loads channel vector col of pixels
+// p0 + row + k * rows, k < KV.  Every load is issued unconditionally (a
+// pixel past the slice re-reads the last pixel) so that all KV are in
+// flight together; `valid` marks the real ones.
+template <int KV>
+__device__ __forceinline__ void load_chunk(const void* __restrict__ x, int64_t P, int vpp,
+                                           int rows, int64_t b, int64_t chunk, int row, int col,
+                                           u32x4 (&v)[KV], bool (&valid)[KV]) {
+    const int64_t p0 = chunk * rows * KV + row;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x) + (b * P) * vpp + col;
+#pragma unroll
+    for (int k = 0; k < KV; ++k) {
+        const int64_t p = p0 + int64_t(k) * rows;
+        valid[k] = p < P;
+        v[k] = src[(p < P ? p : P - 1) * vpp];
+    }
+    // keep the scheduler from moving the first uses above the later loads
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+struct GnArgs {
+    const void* x;
+    void* y;
+    int64_t P;       // pixels per image in the slice
+    int C, vpp, rows, G;
+    int64_t chunks;
+    int64_t n, patch;
+    double count;    // values per (image, group) in the slice
+    float eps;
+    const float* stale_moments;
+    const float* gamma;
+    const float* beta;
+    float* fresh_moments;
+    GnWorkspace ws;
+};
+
+// Statistics and affine of image blockIdx.x from all its chunk sums.  Every
+// global load is issued before any result is needed: the chunk sums, the
+// other patches' stale moments and gamma / beta.
+constexpr int kFinThreads = 512;
+constexpr int kMaxChanPerThread = 8;  // C <= 4096
+
+__global__ __launch_bounds__(kFinThreads) void gn_finalize(GnArgs a) {
+    extern __shared__ double red[];  // [slices][G][2], then (mu, rstd) [G][2]
+    const int64_t b = blockIdx.x;
+    const int tid = threadIdx.x, T = blockDim.x, G = a.G;
+    const int slices = T / G > 0 ? T / G : 1;
+    double* stat = red + 2 * slices * G;
+
+    // gamma / beta of channels tid, tid + T, ...
+    float gam[kMaxChanPerThread], bet[kMaxChanPerThread];
+#pragma unroll
+    for (int u = 0; u < kMaxChanPerThread; ++u) {
+        gam[u] = 1.f;
+        bet[u] = 0.f;
+    }
+    if (a.gamma) {
+#pragma unroll
+        for (int u = 0; u < kMaxChanPerThread; ++u) gam[u] = a.gamma[min(tid + u * T, a.C - 1)];
+    }
+    if (a.beta) {
+#pragma unroll
+        for (int u = 0; u < kMaxChanPerThread; ++u) bet[u] = a.beta[min(tid + u * T, a.C - 1)];
+    }
+    // the other patches' stale moments of group tid (G <= 256 < T): the
+    // first 8 patches' loads go out now, the sum is formed after the chunk
+    // sums' loads are out too
+    const uint64_t* tab = reinterpret_cast<const uint64_t*>(a.stale_moments) + b * a.n * G +
+                          (tid < G ? tid : 0);
+    uint64_t st[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) st[u] = tab[(u < a.n ? u : a.n - 1) * G];
+    // thread (slice, g) adds chunks slice, slice + slices, ... in fp64 (16
+    // loads in flight; the index is clamped and the extra terms dropped by a
+    // select, so the loads need no branches); the slices are then added in
+    // order.
+    const uint64_t* pp = reinterpret_cast<const uint64_t*>(a.ws.partial) + b * a.chunks * G;
+    for (int t = tid; t < slices * G; t += T) {
+        const int g = t % G, sl = t / G;
+        double a1 = 0.0, a2 = 0.0;
+        for (int64_t k0 = sl; k0 < a.chunks; k0 += 16 * int64_t(slices)) {
+            uint64_t w[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int64_t k = k0 + int64_t(u) * slices;
+                w[u] = pp[(k < a.chunks ? k : a.chunks - 1) * G + g];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const bool in = k0 + int64_t(u) * slices < a.chunks;
+                a1 += in ? double(__uint_as_float(uint32_t(w[u]))) : 0.0;
+                a2 += in ? double(__uint_as_float(uint32_t(w[u] >> 32))) : 0.0;
+            }
+        }
+        red[2 * (sl * G + g)] = a1;
+        red[2 * (sl * G + g) + 1] = a2;
+    }
+    double st1 = 0.0, st2 = 0.0;
+    for (int64_t j0 = 0; j0 < a.n; j0 += 8) {
+        if (j0 > 0) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) st[u] = tab[(j0 + u < a.n ? j0 + u : a.n - 1) * G];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool in = j0 + u < a.n && j0 + u != a.patch;
+            st1 += in ? double(__uint_as_float(uint32_t(st[u]))) : 0.0;
+            st2 += in ? double(__uint_as_float(uint32_t(st[u] >> 32))) : 0.0;
+        }
+    }
+    __syncthreads();
+    if (tid < G) {
+        const int g = tid;
+        double s1 = 0.0, s2 = 0.0;
+        for (int sl = 0; sl < slices; ++sl) {
+            s1 += red[2 * (sl * G + g)];
+            s2 += red[2 * (sl * G + g) + 1];
+        }
+        const double m1 = s1 / a.count, m2 = s2 / a.count;
+        a.fresh_moments[(b * G + g) * 2 + 0] = float(m1);
+        a.fresh_moments[(b * G + g) * 2 + 1] = float(m2);
+        const double e1 = (m1 + st1) / double(a.n);
+        const double e2 = (m2 + st2) / double(a.n);
+        double var = e2 - e1 * e1;
+        if (var < 0.0) var = 0.0;
+        stat[2 * g] = e1;
+        stat[2 * g + 1] = 1.0 / sqrt(var + double(a.eps));
+    }
+    __syncthreads();
+    const int cg = a.C / G;
+#pragma unroll
+    for (int u = 0; u < kMaxChanPerThread; ++u) {
+        const int c = tid + u * T;
+        if (c < a.C) {
+            const int g = c / cg;
+            const double aa = stat[2 * g + 1] * double(gam[u]);
+            a.ws.affine[(b * a.C + c) * 2 + 0] = float(aa);
+            a.ws.affine[(b * a.C + c) * 2 + 1] = float(double(bet[u]) - stat[2 * g] * aa);
+        }
+    }
+}
+
+template <class T, int KV>
+__global__ __launch_bounds__(kMaxThreads) void gn_moments(GnArgs a) {
+    extern __shared__ float lds[];  // [2][rows][C]
     const int64_t b = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x;
-    const int col = tid % vpp, row = tid / vpp;
-    const int64_t p0 = chunk * ppc;
-    const int64_t p1 = p0 + ppc < P ? p0 + ppc : P;
+    const int C = a.C, rows = a.rows, G = a.G;
+    const int col = tid % a.vpp, row = tid / a.vpp;
+    u32x4 v[KV];
+    bool valid[KV];
+    load_chunk<KV>(a.x, a.P, a.vpp, rows, b, chunk, row, col, v, valid);
     float s[T::VEC], ss[T::VEC];
 #pragma unroll
     for (int j = 0; j < T::VEC; ++j) s[j] = ss[j] = 0.f;
-    const u32x4* base = reinterpret_cast<const u32x4*>(x + b * P * C) + col;
-    // kUnroll independent 16-byte loads in flight per thread
-    for (int64_t p = p0 + row; p < p1; p += int64_t(kUnroll) * rows) {
-        u32x4 v[kUnroll];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t pu = p + int64_t(u) * rows;
-            v[u] = pu < p1 ? base[pu * vpp] : u32x4{0, 0, 0, 0};
-        }
+    for (int k = 0; k < KV; ++k) {
+        float f[T::VEC];
+        T::unpack(v[k], f);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            float f[T::VEC];
-            T::unpack(v[u], f);
-#pragma unroll
-            for (int j = 0; j < T::VEC; ++j) {
-                s[j] += f[j];
-                ss[j] = fmaf(f[j], f[j], ss[j]);
-            }
+        for (int j = 0; j < T::VEC; ++j) {
+            const float e = valid[k] ? f[j] : 0.f;
+            s[j] += e;
+            ss[j] = fmaf(e, e, ss[j]);
         }
     }
+    // C * row + VEC * col floats is a multiple of 16 bytes
 #pragma unroll
-    for (int j = 0; j < T::VEC; ++j) {
-        lds[row * C + col * T::VEC + j] = s[j];
-        lds[rows * C + row * C + col * T::VEC + j] = ss[j];
+    for (int q = 0; q < T::VEC / 4; ++q) {
+        *reinterpret_cast<f32x4*>(&lds[row * C + col * T::VEC + 4 * q]) =
+            f32x4{s[4 * q], s[4 * q + 1], s[4 * q + 2], s[4 * q + 3]};
+        *reinterpret_cast<f32x4*>(&lds[rows * C + row * C + col * T::VEC + 4 * q]) =
+            f32x4{ss[4 * q], ss[4 * q + 1], ss[4 * q + 2], ss[4 * q + 3]};
     }
     __syncthreads();
-    // channel totals over the block's rows (fixed order)
-    float* tot = lds + 2 * rows * C;
+    // channel totals over the block's rows (fixed order), into row 0
     for (int t = tid; t < 2 * C; t += blockDim.x) {
         const int stat = t / C, c = t % C;
-        float acc = 0.f;
-        for (int r = 0; r < rows; ++r) acc += lds[stat * rows * C + r * C + c];
-        tot[stat * C + c] = acc;
+        float* col0 = lds + stat * rows * C + c;
+        float acc = col0[0];
+        for (int r = 1; r < rows; ++r) acc += col0[r * C];
+        col0[0] = acc;
     }
     __syncthreads();
     const int cg = C / G;
     for (int task = tid; task < 2 * G; task += blockDim.x) {
         const int g = task >> 1, stat = task & 1;
-        const float* src = tot + stat * C + g * cg;
+        const float* src = lds + stat * rows * C + g * cg;
         float acc = 0.f;
         for (int c = 0; c < cg; ++c) acc += src[c];
-        partial[((b * chunks + chunk) * G + g) * 2 + stat] = acc;
+        a.ws.partial[((b * a.chunks + chunk) * G + g) * 2 + stat] = acc;
     }
 }
 
-// One block per (group, image): fixed-order fp64 reduction of the chunk
-// partials, the fresh/stale mix and the clamp, then the per-channel affine.
-__global__ __launch_bounds__(256) void gn_finalize(const float* __restrict__ partial,
-                                                   int64_t chunks, int C, int G, int64_t n,
-                                                   int64_t patch, double count, float eps,
-                                                   const float* __restrict__ stale_moments,
-                                                   const float* __restrict__ gamma,
-                                                   const float* __restrict__ beta,
-                                                   float* __restrict__ fresh_moments,
-                                                   float* __restrict__ affine) {
-    __shared__ double red[2][256];
-    __shared__ double stats[2];
-    const int g = blockIdx.x;
-    const int64_t b = blockIdx.y;
-    const int tid = threadIdx.x;
-    double s1 = 0.0, s2 = 0.0;
-    const float* pp = partial + (b * chunks * G + g) * 2;
-    for (int64_t k = tid; k < chunks; k += 256) {
-        s1 += double(pp[k * G * 2 + 0]);
-        s2 += double(pp[k * G * 2 + 1]);
-    }
-    red[0][tid] = s1;
-    red[1][tid] = s2;
-    __syncthreads();
-    for (int w = 128; w > 0; w >>= 1) {
-        if (tid < w) {
-            red[0][tid] += red[0][tid + w];
-            red[1][tid] += red[1][tid + w];
-        }
-        __syncthreads();
-    }
-    if (tid == 0) {
-        const double m1 = red[0][0] / count, m2 = red[1][0] / count;
-        fresh_moments[(b * G + g) * 2 + 0] = float(m1);
-        fresh_moments[(b * G + g) * 2 + 1] = float(m2);
-        double e1 = m1, e2 = m2;
-        for (int64_t j = 0; j < n; ++j) {
-            if (j == patch) continue;
-            e1 += double(stale_moments[((b * n + j) * G + g) * 2 + 0]);
-            e2 += double(stale_moments[((b * n + j) * G + g) * 2 + 1]);
-        }
-        e1 /= double(n);
-        e2 /= double(n);
-        double var = e2 - e1 * e1;
-        if (var < 0.0) var = 0.0;
-        stats[0] = e1;
-        stats[1] = 1.0 / sqrt(var + double(eps));
-    }
-    __syncthreads();
-    const int cg = C / G;
-    const double mu = stats[0], rstd = stats[1];
-    for (int c = g * cg + tid; c < (g + 1) * cg; c += 256) {
-        const double ga = gamma ? double(gamma[c]) : 1.0;
-        const double be = beta ? double(beta[c]) : 0.0;
-        const double a = rstd * ga;
-        affine[(b * C + c) * 2 + 0] = float(a);
-        affine[(b * C + c) * 2 + 1] = float(be - mu * a);
-    }
-}
-
-template <class T>
-__global__ __launch_bounds__(1024) void gn_normalize(const typename T::elem* __restrict__ x,
-                                                     typename T::elem* __restrict__ y, int64_t P,
-                                                     int C, int vpp, int rows, int64_t ppc,
-                                                     const float* __restrict__ affine) {
+template <class T, int KV>
+__global__ __launch_bounds__(kMaxThreads) void gn_normalize(GnArgs a) {
     const int64_t b = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x;
-    const int col = tid % vpp, row = tid / vpp;
-    float a[T::VEC], c0[T::VEC];
-    const float* af = affine + (b * C + col * T::VEC) * 2;
+    const int col = tid % a.vpp, row = tid / a.vpp;
+    u32x4 v[KV];
+    bool valid[KV];
+    load_chunk<KV>(a.x, a.P, a.vpp, a.rows, b, chunk, row, col, v, valid);
+    // (a_c, b_c) of this thread's VEC channels: VEC/2 16-byte loads
+    const f32x4* af = reinterpret_cast<const f32x4*>(a.ws.affine + (b * a.C + col * T::VEC) * 2);
+    f32x4 ab[T::VEC / 2];
 #pragma unroll
-    for (int j = 0; j < T::VEC; ++j) {
-        a[j] = af[2 * j];
-        c0[j] = af[2 * j + 1];
-    }
-    const int64_t p0 = chunk * ppc;
-    const int64_t p1 = p0 + ppc < P ? p0 + ppc : P;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + b * P * C) + col;
-    u32x4* dst = reinterpret_cast<u32x4*>(y + b * P * C) + col;
-    for (int64_t p = p0 + row; p < p1; p += int64_t(kUnroll) * rows) {
-        u32x4 v[kUnroll];
+    for (int q = 0; q < T::VEC / 2; ++q) ab[q] = af[q];
+    const int64_t p0 = chunk * a.rows * KV + row;
+    u32x4* dst = reinterpret_cast<u32x4*>(a.y) + (b * a.P) * a.vpp + col;
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t pu = p + int64_t(u) * rows;
-            if (pu < p1) v[u] = src[pu * vpp];
-        }
+    for (int k = 0; k < KV; ++k) {
+        if (valid[k]) {
+            float f[T::VEC];
+            T::unpack(v[k], f);
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int64_t pu = p + int64_t(u) * rows;
-            if (pu < p1) {
-                float f[T::VEC];
-                T::unpack(v[u], f);
-#pragma unroll
-                for (int j = 0; j < T::VEC; ++j) f[j] = fmaf(f[j], a[j], c0[j]);
-                dst[pu * vpp] = T::pack(f);
-            }
+            for (int j = 0; j < T::VEC; ++j)
+                f[j] = fmaf(f[j], ab[j / 2][2 * (j % 2)], ab[j / 2][2 * (j % 2) + 1]);
+            __builtin_nontemporal_store(T::pack(f), dst + (p0 + int64_t(k) * a.rows) * a.vpp);
         }
     }
+}
+
+template <class T, int KV>
+hipError_t run_kv(const GnPlan& p, const GnArgs& a, int64_t B, hipStream_t s) {
+    dim3 grid(unsigned(p.chunks), unsigned(B));
+    const size_t lds = size_t(2) * p.rows * a.C * sizeof(float);
+    hipLaunchKernelGGL((gn_moments<T, KV>), grid, dim3(p.threads), lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int slices = kFinThreads / a.G;
+    const size_t lds_fin = (size_t(slices) * 2 * a.G + 2 * a.G) * sizeof(double);
+    hipLaunchKernelGGL(gn_finalize, dim3(unsigned(B)), dim3(kFinThreads), lds_fin, s, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((gn_normalize<T, KV>), grid, dim3(p.threads), 0, s, a);
+    return hipGetLastError();
 }
 
 template <class T>
@@ -227,33 +325,37 @@ hipError_t run(const Geom& g, int64_t C, int64_t G, float eps, const void* x,
                const float* stale_moments, const float* gamma, const float* beta, void* y,
                float* fresh_moments, void* ws, hipStream_t s) {
     const GnPlan p = plan_gn(g, C, int(sizeof(typename T::elem)));
-    const int64_t P = g.h() * g.W;
-    float* partial = static_cast<float*>(ws);
-    float* affine = partial + g.B * p.chunks * G * 2;
-    const size_t lds = size_t(2) * (p.rows + 1) * C * sizeof(float);
-    dim3 grid(unsigned(p.chunks), unsigned(g.B));
-    hipLaunchKernelGGL(gn_moments<T>, grid, dim3(p.threads), lds, s,
-                       static_cast<const typename T::elem*>(x), P, int(C), p.vpp, p.rows, int(G),
-                       p.ppc, p.chunks, partial);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gn_finalize, dim3(unsigned(G), unsigned(g.B)), dim3(256), 0, s, partial, p.chunks,
-                       int(C), int(G), g.n, g.i, double(P) * double(C / G), eps, stale_moments,
-                       gamma, beta, fresh_moments, affine);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gn_normalize<T>, grid, dim3(p.threads), 0, s,
-                       static_cast<const typename T::elem*>(x),
-                       static_cast<typename T::elem*>(y), P, int(C), p.vpp, p.rows, p.ppc,
-                       affine);
-    return hipGetLastError();
+    GnArgs a;
+    a.x = x;
+    a.y = y;
+    a.P = g.h() * g.W;
+    a.C = int(C);
+    a.vpp = p.vpp;
+    a.rows = p.rows;
+    a.G = int(G);
+    a.chunks = p.chunks;
+    a.n = g.n;
+    a.patch = g.i;
+    a.count = double(a.P) * double(C / G);
+    a.eps = eps;
+    a.stale_moments = stale_moments;
+    a.gamma = gamma;
+    a.beta = beta;
+    a.fresh_moments = fresh_moments;
+    a.ws = carve(ws, g, p, C, G);
+    switch (p.kv) {
+        case 1: return run_kv<T, 1>(p, a, g.B, s);
+        case 2: return run_kv<T, 2>(p, a, g.B, s);
+        case 4: return run_kv<T, 4>(p, a, g.B, s);
+        case 8: return run_kv<T, 8>(p, a, g.B, s);
+        default: return run_kv<T, kMaxKV>(p, a, g.B, s);
+    }
 }
 
 }  // namespace
 
 size_t groupnorm_workspace_bytes(const Geom& g, int64_t C, int64_t G, int elem_bytes) {
-    const GnPlan p = plan_gn(g, C, elem_bytes);
-    return size_t(g.B * p.chunks * G * 2 + g.B * C * 2) * sizeof(float);
+    return workspace_bytes(g, plan_gn(g, C, elem_bytes), C, G);
 }
 
 hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool bf16,

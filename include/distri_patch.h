@@ -148,7 +148,8 @@ int distri_patch_conv3x3_halo(const distri_patch_geom *g, int64_t c_in, int64_t 
  *   workspace       >= distri_async_groupnorm_workspace_size() bytes;
  *                   contents on entry are ignored
  * C must be a multiple of 8 for bf16 and of 4 for fp32, and at most 4096
- * (bf16) / 2048 (fp32) (DISTRI_ERR_UNSUPPORTED).
+ * (bf16) / 2048 (fp32); G at most 256 (DISTRI_ERR_UNSUPPORTED).  The
+ * result is deterministic (fixed summation order, no atomics).
  */
 int distri_async_groupnorm_workspace_size(const distri_patch_geom *g, int64_t channels,
                                           int64_t groups, int dtype, size_t *bytes);

@@ -103,6 +103,8 @@ def test_groupnorm_rejects_bad_arguments(lib):
     assert n.value > 0
     assert lib.distri_async_groupnorm_workspace_size(G(*g), 640, 33, BF16, ctypes.byref(n)) == SHAPE
     assert lib.distri_async_groupnorm_workspace_size(G(*g), 644, 4, BF16, ctypes.byref(n)) == UNSUP
+    assert lib.distri_async_groupnorm_workspace_size(G(*g), 2048, 512, BF16, ctypes.byref(n)) == UNSUP
+    assert lib.distri_async_groupnorm_workspace_size(G(*g), 2048, 256, BF16, ctypes.byref(n)) == OK
     assert lib.distri_async_groupnorm_workspace_size(G(*g), 640, 32, BF16, None) == NULL
     x, tab, gam, bet, y, fm, ws = (A + k * 64 * MB for k in range(7))
 

@@ -232,3 +232,51 @@ def test_extreme_scores_stay_finite():
     g = gpu_copy(d)
     out = _run_attention(wl, g)
     assert_close(to_np(out), _oracle_attention(wl, d), "bf16", "attention large logits")
+
+
+# GroupNorm launch shapes away from the SDXL ones: groups that split a
+# 16-byte channel vector (C/G = 4), one group, block widths that are not a
+# power of two (C = 40 -> 5 vectors per pixel), fp32, and more chunks than
+# one block row covers.
+GN_SHAPES = [si.Workload("gn_c40_g5", 2, 40, 12, 10, 3, 1, groups=5, seed=3001, patch=1),
+             si.Workload("gn_c1024_g256", 1, 1024, 8, 6, 2, 1, groups=256, seed=3002, patch=1),
+             si.Workload("gn_c64_g1", 3, 64, 16, 9, 4, 1, groups=1, seed=3003, patch=3),
+             si.Workload("gn_f32_c12_g3", 2, 12, 10, 11, 5, 1, groups=3, dtype="f32", sigma=0.05,
+                         seed=3004, patch=2),
+             si.Workload("gn_c2048_g32", 3, 2048, 32, 24, 4, 1, groups=32, seed=3005, patch=0)]
+
+
+@pytest.mark.parametrize("wl", GN_SHAPES, ids=[w.name for w in GN_SHAPES])
+def test_groupnorm_shapes(wl):
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    yg, fm = dp.distri_async_groupnorm(wl.geom, wl.groups, g["x_fresh"], g["table"], g["gamma"],
+                                       g["beta"], eps=wl.eps)
+    ref_y, ref_fm = oracle.async_groupnorm(wl.geom, wl.channels, wl.groups, wl.eps, d["x_fresh"],
+                                           d["table"].double().numpy(), d["gamma"], d["beta"])
+    assert_close(to_np(yg), ref_y, wl.dtype, f"groupnorm {wl.name}")
+    fmn = to_np(fm)
+    assert np.all(np.abs(fmn[..., 0] - ref_fm[..., 0]) <= 1e-5 * np.sqrt(ref_fm[..., 1]) + 1e-7)
+    assert np.all(np.abs(fmn[..., 1] - ref_fm[..., 1]) <= 1e-5 * ref_fm[..., 1] + 1e-7)
+
+
+def test_groupnorm_reused_workspace_is_exact():
+    """The GroupNorm workspace carries per-call flags between its two
+    launches; reusing one workspace (also after filling it with arbitrary
+    bytes) across calls on different inputs must give the same bits as a
+    fresh zeroed workspace each time."""
+    wl = W["sdxl1024_l2"].with_patch(3)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    nb = dp.distri_async_groupnorm_workspace_size(wl.geom, wl.channels, wl.groups, dp.DISTRI_BF16)
+    shared = torch.randint(0, 255, (nb,), dtype=torch.uint8, device="cuda")
+    for k in range(3):
+        x = (g["x_fresh"].float() * (1.0 + 0.5 * k) + 0.25 * k).to(torch.bfloat16)
+        ref_y, ref_fm = dp.distri_async_groupnorm(
+            wl.geom, wl.groups, x, g["table"], g["gamma"], g["beta"],
+            workspace=torch.zeros(nb, dtype=torch.uint8, device="cuda"))
+        y, fm = dp.distri_async_groupnorm(wl.geom, wl.groups, x, g["table"], g["gamma"], g["beta"],
+                                          workspace=shared)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)), f"call {k}"
+        assert torch.equal(fm, ref_fm), f"call {k}"
