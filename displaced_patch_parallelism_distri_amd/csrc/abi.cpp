@@ -11,6 +11,22 @@
 
 #include "dp_common.h"
 
+namespace dp {
+
+int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return -1;
+    if (dev < 64) cached[dev] = cus;
+    return cus;
+}
+
+}  // namespace dp
+
 namespace {
 
 thread_local char g_last_error[256] = "";
@@ -177,9 +193,14 @@ int distri_patch_conv3x3_halo(const distri_patch_geom* g, int64_t c_in, int64_t 
     if (st) return st;
     DP_CHECK(c_in >= 1 && c_out >= 1, DISTRI_ERR_SHAPE, "c_in and c_out must be >= 1");
     DP_CHECK(c_in <= 65536 && c_out <= 65536, DISTRI_ERR_UNSUPPORTED, "channels above 65536");
-    if (dtype == DISTRI_BF16)
-        DP_CHECK(c_in % 32 == 0, DISTRI_ERR_UNSUPPORTED, "bf16 conv needs c_in % 32 == 0");
     const dp::Geom gg = to_geom(g);
+    if (dtype == DISTRI_BF16) {
+        DP_CHECK(c_in % 64 == 0, DISTRI_ERR_UNSUPPORTED, "bf16 conv needs c_in % 64 == 0");
+        DP_CHECK(gg.B * gg.H * gg.W * c_in < (int64_t(1) << 31) &&
+                     gg.B * gg.H * gg.W * c_out < (int64_t(1) << 31) &&
+                     c_out * 9 * c_in < (int64_t(1) << 31),
+                 DISTRI_ERR_UNSUPPORTED, "bf16 conv tensors must stay below 2^31 elements");
+    }
     const size_t eb = size_t(elem_bytes_of(dtype));
     const size_t ybytes = size_t(gg.B * gg.h() * gg.W * c_out) * eb;
     if (ybytes == 0) return DISTRI_OK;

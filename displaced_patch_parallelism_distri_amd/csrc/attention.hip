@@ -435,18 +435,6 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     *reinterpret_cast<u32x4*>(op) = w;
 }
 
-int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-        return -1;
-    if (dev < 64) cached[dev] = cus;
-    return cus;
-}
-
 // ----------------------------------------------------------------- fp32 path
 struct AttnArgsF32 {
     const float* q;

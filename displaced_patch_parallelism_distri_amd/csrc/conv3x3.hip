@@ -11,23 +11,36 @@
 // image is zero.
 //
 // bf16 kernel: implicit GEMM on MFMA with M = B*h*W output pixels, N = Cout,
-// K = 9*Cin ordered (kh, kw, ci).  A block computes a 128 x 128 (pixel x
-// cout) tile with 4 waves of 64 x 64 (2 x 2 v_mfma_f32_32x32x16_bf16 tiles).
-// K advances 32 channels of one tap at a time; the A tile rows are gathered
-// per pixel from the fresh slice, the stale halo row or zero, as 16-byte
-// channel vectors (NHWC keeps a pixel's channels contiguous) - the halo is
-// never materialised.  The weight tile comes from [Cout][3][3][Cin], which
-// is already K-contiguous per output channel.  Both tiles are staged in
-// double-buffered LDS.
+// K = 9*Cin ordered (kh, kw, ci).  A block computes a BM x 160 (pixel x
+// cout) tile with 4 waves in a 2 x 2 grid of (BM/2) x 80 wave tiles made of
+// v_mfma_f32_16x16x32_bf16 tiles.  Cout = 640 and 1280 are 4 and 8 tiles
+// of 160; BM (128 or 64) is picked per shape so that the grid gives about
+// two blocks per CU (two blocks are resident per CU).
+//  * K advances 64 channels of one tap per step.  The A rows are gathered
+//    per pixel from the fresh slice, the stale halo row or zero (NHWC keeps a
+//    pixel's channels contiguous, so a row is 8 x 16-byte vectors); the halo
+//    is never materialised.  A thread's source pixels are decoded once; the
+//    three row sources are re-selected only when the tap changes.
+//  * The weight tile comes from [Cout][3][3][Cin], already K-contiguous per
+//    output channel.
+//  * Both tiles go global -> registers -> LDS, double-buffered: the loads of
+//    step s+1 are in flight while step s computes; one barrier per step.
+//    LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
+//    (row / 2) % 8, which keeps the ds_read_b128 operand reads and the
+//    stores free of bank conflicts without padding (2 x 72 KB fit per CU).
+//  * Blocks are remapped so that each XCD works through the tiles of one or
+//    two cout slices: their weights stay in that XCD's L2.
 // fp32 kernel: one thread per output element, direct sum; parity-grade.
 #include "dp_common.h"
+
+#include <type_traits>
 
 namespace dp {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int APITCH = BK + 8;  // LDS row pitch (bf16 elements): 80 bytes
-constexpr int BPITCH = BK + 8;
+constexpr int BN = 160, BK = 64;
+constexpr int WN = 80, NT = WN / 16;  // wave tile columns, 16-wide MFMA tiles
+constexpr int B_CHUNKS = BN * 8 / 256;  // 16-byte chunks per thread per step
 
 struct ConvArgs {
     const uint16_t* xf;
@@ -35,129 +48,186 @@ struct ConvArgs {
     const uint16_t* w;
     const float* bias;
     uint16_t* y;
-    int64_t M;  // B*h*W
-    int64_t h, W, H;
-    int64_t n, i;
+    int M;  // B*h*W
+    int h, W, H;
+    int n, i;
     int cin, cout;
+    int mtiles, ntiles;
 };
 
-// Pointer to channel ci0 of hybrid-map pixel (b, local row rr, col cc), or
-// nullptr where the padding is zero.
-__device__ __forceinline__ const uint16_t* pixel_ptr(const ConvArgs& a, int64_t b, int64_t rr,
-                                                     int64_t cc) {
-    if (cc < 0 || cc >= a.W) return nullptr;
-    if (rr >= 0 && rr < a.h) return a.xf + ((b * a.h + rr) * a.W + cc) * a.cin;
-    if (rr == -1) {
-        if (a.i == 0) return nullptr;
-        return a.xs + ((b * a.H + a.i * a.h - 1) * a.W + cc) * a.cin;
-    }
-    if (a.i == a.n - 1) return nullptr;
-    return a.xs + ((b * a.H + (a.i + 1) * a.h) * a.W + cc) * a.cin;
-}
+// 16-byte chunk position of chunk `c` of LDS row `r`
+__device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+template <int BM>
 __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * APITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][BN * BPITCH];
+    constexpr int WM = BM / 2, MT = WM / 16;
+    constexpr int A_CHUNKS = BM * 8 / 256;
+    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][BN * BK];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 31, g = lane >> 5;
+    const int l16 = lane & 15, lq = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
-    const int64_t m0 = int64_t(blockIdx.x) * BM;
-    const int n0 = int(blockIdx.y) * BN;
 
-    // loader mapping: chunk id = tid + 256*j -> row id>>2, channel group id&3
-    int64_t pb[2], pr[2], pc[2];
-    bool pvalid[2];
-    int lrow[2], lc4[2];
+    // XCD-aware tile order: logical tiles run cout-slice-major; the blocks
+    // of one XCD (physical id % 8) take a contiguous logical range
+    const int ntot = a.mtiles * a.ntiles;
+    const int n8 = ntot - ntot % 8;
+    const int pw = blockIdx.x;
+    const int logical = pw < n8 ? (pw % 8) * (n8 / 8) + pw / 8 : pw;
+    const int nt = logical / a.mtiles, mt = logical % a.mtiles;
+    const int m0 = mt * BM, n0 = nt * BN;
+
+    // ---- A loader: chunk c = tid + 256 j -> row c / 8, 16-byte chunk c % 8
+    int ab[A_CHUNKS], ar[A_CHUNKS], acol[A_CHUNKS];
+    bool avalid[A_CHUNKS];
+    const int akc = tid & 7;
+    const int hw = a.h * a.W;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int id = tid + 256 * j;
-        lrow[j] = id >> 2;
-        lc4[j] = id & 3;
-        const int64_t m = m0 + lrow[j];
-        pvalid[j] = m < a.M;
-        const int64_t mm = pvalid[j] ? m : 0;
-        const int64_t hw = a.h * a.W;
-        pb[j] = mm / hw;
-        pr[j] = (mm % hw) / a.W;
-        pc[j] = mm % a.W;
+    for (int j = 0; j < A_CHUNKS; ++j) {
+        const int row = (tid >> 3) + 32 * j;
+        const int m = m0 + row;
+        avalid[j] = m < a.M;
+        const int mm = avalid[j] ? m : 0;
+        ab[j] = mm / hw;
+        const int rem = mm - ab[j] * hw;
+        ar[j] = rem / a.W;
+        acol[j] = rem - ar[j] * a.W;
     }
-    const int cin = a.cin;
-    const int kchunks = cin / BK;
-    const int nk = 9 * kchunks;
-
-    u32x4 ar[2], br[2];
-    auto gload = [&](int k) {
-        const int tap = k / kchunks;
-        const int ci0 = (k - tap * kchunks) * BK;
+    const uint16_t* aptr[A_CHUNKS];  // pixel base of the current tap (or x_fresh)
+    bool aok[A_CHUNKS];
+    auto set_tap = [&](int tap) {
         const int kh = tap / 3, kw = tap - kh * 3;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint16_t* p =
-                pvalid[j] ? pixel_ptr(a, pb[j], pr[j] + kh - 1, pc[j] + kw - 1) : nullptr;
-            ar[j] = p ? *reinterpret_cast<const u32x4*>(p + ci0 + lc4[j] * 8) : u32x4{0, 0, 0, 0};
-            const int n = n0 + lrow[j];
-            br[j] = n < a.cout ? *reinterpret_cast<const u32x4*>(
-                                     a.w + (int64_t(n) * 9 + tap) * cin + ci0 + lc4[j] * 8)
-                               : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            *reinterpret_cast<u32x4*>(&a_lds[buf][lrow[j] * APITCH + lc4[j] * 8]) = ar[j];
-            *reinterpret_cast<u32x4*>(&b_lds[buf][lrow[j] * BPITCH + lc4[j] * 8]) = br[j];
+        for (int j = 0; j < A_CHUNKS; ++j) {
+            const int rr = ar[j] + kh - 1, cc = acol[j] + kw - 1;
+            bool ok = avalid[j] && cc >= 0 && cc < a.W;
+            const uint16_t* p = a.xf;
+            if (rr >= 0 && rr < a.h) {
+                p = a.xf + ((size_t(ab[j]) * a.h + rr) * a.W + cc) * a.cin;
+            } else if (rr < 0) {
+                ok = ok && a.i > 0;
+                p = a.xs + ((size_t(ab[j]) * a.H + size_t(a.i) * a.h - 1) * a.W + cc) * a.cin;
+            } else {
+                ok = ok && a.i < a.n - 1;
+                p = a.xs + ((size_t(ab[j]) * a.H + size_t(a.i + 1) * a.h) * a.W + cc) * a.cin;
+            }
+            aok[j] = ok;
+            aptr[j] = ok ? p : a.xf;
         }
     };
 
-    f32x16 acc[2][2];
+    // ---- B loader: chunk c = tid + 256 j -> weight row c / 8, chunk c % 8
+    const uint16_t* bptr[B_CHUNKS];
+    bool bok[B_CHUNKS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int k = 0; k < nk; ++k) {
-        const int cur = k & 1;
-        if (k + 1 < nk) gload(k + 1);
-#pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            bf16x8 av[2], bv[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-                av[i] = *reinterpret_cast<const bf16x8*>(
-                    &a_lds[cur][(wm * 64 + i * 32 + lr) * APITCH + ks * 16 + g * 8]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-                bv[j] = *reinterpret_cast<const bf16x8*>(
-                    &b_lds[cur][(wn * 64 + j * 32 + lr) * BPITCH + ks * 16 + g * 8]);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[j], acc[i][j],
-                                                                        0, 0, 0);
-        }
-        if (k + 1 < nk) lstore(cur ^ 1);
-        __syncthreads();
+    for (int j = 0; j < B_CHUNKS; ++j) {
+        const int row = (tid >> 3) + 32 * j;
+        bok[j] = n0 + row < a.cout;
+        bptr[j] = a.w + size_t(bok[j] ? n0 + row : 0) * 9 * a.cin + akc * 8;
     }
 
-    // epilogue: acc[i][j][e] is pixel m0 + wm*64 + i*32 + 8*(e/4) + 4g + e%4,
-    // cout n0 + wn*64 + j*32 + lr
+    const int kchunks = a.cin / BK;
+    const int nsteps = 9 * kchunks;
+    // Two register sets: the loads of step s + 2 are issued while step s
+    // computes, and step s + 1's values (loaded a step earlier) are stored to
+    // LDS at the end of step s.  Loaded values stay raw until they are
+    // stored: the zero select for padding / out-of-range rows is applied
+    // there, so nothing waits on the loads while the MFMAs run.
+    u32x4 areg[2][A_CHUNKS], breg[2][B_CHUNKS];
+    bool amask[2][A_CHUNKS];
+    auto gload = [&](int s, auto set) {
+        constexpr int R = decltype(set)::value;
+        const int tap = s / kchunks;
+        const int ci0 = (s - tap * kchunks) * BK;
+        if (ci0 == 0) set_tap(tap);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int n = n0 + wn * 64 + j * 32 + lr;
+        for (int j = 0; j < A_CHUNKS; ++j) {
+            areg[R][j] = *reinterpret_cast<const u32x4*>(aptr[j] + ci0 + akc * 8);
+            amask[R][j] = aok[j];
+        }
+#pragma unroll
+        for (int j = 0; j < B_CHUNKS; ++j)
+            breg[R][j] = *reinterpret_cast<const u32x4*>(bptr[j] + tap * a.cin + ci0);
+    };
+    auto lstore = [&](int buf, auto set) {
+        constexpr int R = decltype(set)::value;
+#pragma unroll
+        for (int j = 0; j < A_CHUNKS; ++j) {
+            const int row = (tid >> 3) + 32 * j;
+            *reinterpret_cast<u32x4*>(&a_lds[buf][row * BK + swz(row, akc) * 8]) =
+                amask[R][j] ? areg[R][j] : u32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int j = 0; j < B_CHUNKS; ++j) {
+            const int row = (tid >> 3) + 32 * j;
+            *reinterpret_cast<u32x4*>(&b_lds[buf][row * BK + swz(row, akc) * 8]) =
+                bok[j] ? breg[R][j] : u32x4{0, 0, 0, 0};
+        }
+    };
+
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int i = 0; i < MT; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int cur) {
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk) {
+            bf16x8 af[MT], bf[NT];
+#pragma unroll
+            for (int i = 0; i < MT; ++i) {
+                const int row = wm * WM + i * 16 + l16;
+                af[i] = *reinterpret_cast<const bf16x8*>(&a_lds[cur][row * BK + swz(row, kk * 4 + lq) * 8]);
+            }
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                const int row = wn * WN + j * 16 + l16;
+                bf[j] = *reinterpret_cast<const bf16x8*>(&b_lds[cur][row * BK + swz(row, kk * 4 + lq) * 8]);
+            }
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int j = 0; j < NT; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    // step s computes LDS buffer s % 2 from register set s % 2's data
+    auto step = [&](int s, auto set) {
+        constexpr int R = decltype(set)::value;
+        constexpr int Rn = R ^ 1;
+        if (s + 2 < nsteps) gload(s + 2, set);
+        compute(R);
+        if (s + 1 < nsteps) lstore(Rn, std::integral_constant<int, Rn>());
+        __syncthreads();
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    gload(0, S0());
+    if (nsteps > 1) gload(1, S1());
+    lstore(0, S0());
+    __syncthreads();
+    for (int s = 0; s < nsteps; s += 2) {
+        step(s, S0());
+        if (s + 1 < nsteps) step(s + 1, S1());
+    }
+
+    // epilogue: acc[i][j][e] is pixel m0 + wm*WM + i*16 + 4*lq + e,
+    // cout n0 + wn*80 + j*16 + l16
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int n = n0 + wn * WN + j * 16 + l16;
         if (n >= a.cout) continue;
         const float bias = a.bias ? a.bias[n] : 0.f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < MT; ++i)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int64_t m = m0 + wm * 64 + i * 32 + 8 * (e >> 2) + 4 * g + (e & 3);
-                if (m < a.M) a.y[m * a.cout + n] = f32_to_bf16(acc[i][j][e] + bias);
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm * WM + i * 16 + 4 * lq + e;
+                if (m < a.M) a.y[size_t(m) * a.cout + n] = f32_to_bf16(acc[i][j][e] + bias);
             }
     }
 }
@@ -217,16 +287,25 @@ hipError_t launch_conv3x3(const Geom& g, int64_t cin, int64_t cout, bool bf16, c
         a.w = static_cast<const uint16_t*>(w);
         a.bias = bias;
         a.y = static_cast<uint16_t*>(y);
-        a.M = M;
-        a.h = g.h();
-        a.W = g.W;
-        a.H = g.H;
-        a.n = g.n;
-        a.i = g.i;
+        a.M = int(M);
+        a.h = int(g.h());
+        a.W = int(g.W);
+        a.H = int(g.H);
+        a.n = int(g.n);
+        a.i = int(g.i);
         a.cin = int(cin);
         a.cout = int(cout);
-        dim3 grid(unsigned(ceil_div(M, BM)), unsigned(ceil_div(cout, BN)));
-        hipLaunchKernelGGL(conv_bf16_kernel, grid, dim3(256), 0, s, a);
+        a.ntiles = int(ceil_div(cout, BN));
+        // two blocks are resident per CU: take the 128-row tile only when
+        // it still gives at least ~1.6 blocks per CU
+        const int64_t t128 = ceil_div(M, 128) * a.ntiles;
+        const bool big = t128 * 10 >= int64_t(device_cus()) * 16;
+        a.mtiles = int(ceil_div(M, big ? 128 : 64));
+        const unsigned grid = unsigned(a.mtiles) * unsigned(a.ntiles);
+        if (big)
+            hipLaunchKernelGGL(conv_bf16_kernel<128>, dim3(grid), dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(conv_bf16_kernel<64>, dim3(grid), dim3(256), 0, s, a);
         return hipGetLastError();
     }
     ConvArgsF32 a;
@@ -250,3 +329,4 @@ hipError_t launch_conv3x3(const Geom& g, int64_t cin, int64_t cout, bool bf16, c
 }
 
 }  // namespace dp
+

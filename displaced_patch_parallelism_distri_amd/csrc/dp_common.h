@@ -81,6 +81,9 @@ struct Geom {
     int64_t L() const { return H * W; }
 };
 
+// Compute units of the current device (cached per device), or -1.
+int device_cus();
+
 hipError_t launch_refresh(const Geom& g, int64_t row_elems, int elem_bytes, const void* fresh,
                           void* stale, hipStream_t s);
 

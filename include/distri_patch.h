@@ -120,7 +120,8 @@ int distri_patch_self_attn(const distri_patch_geom *g, int64_t heads, int64_t he
  *   weight   [Cout, 3, 3, Cin]    dtype
  *   bias     [Cout] fp32 or NULL
  *   y        [B, h, W, Cout]      dtype
- * bf16 requires Cin % 32 == 0 (DISTRI_ERR_UNSUPPORTED); any Cout.
+ * bf16 requires Cin % 64 == 0, and B*H*W*Cin, B*H*W*Cout and Cout*9*Cin below
+ * 2^31 (DISTRI_ERR_UNSUPPORTED); any Cout.
  */
 int distri_patch_conv3x3_halo(const distri_patch_geom *g, int64_t c_in, int64_t c_out,
                               int dtype, const void *x_fresh, const void *x_stale,

@@ -86,7 +86,8 @@ def test_conv_rejects_bad_arguments(lib):
     g = (2, 240, 240, 8, 4)
     assert conv(lib, (2, 241, 240, 8, 4)) == SHAPE
     assert conv(lib, (2, 240, 240, 8, 9)) == SHAPE
-    assert conv(lib, g, cin=48) == UNSUP                  # bf16 needs c_in % 32
+    assert conv(lib, g, cin=48) == UNSUP                  # bf16 needs c_in % 64
+    assert conv(lib, g, cin=96) == UNSUP
     assert conv(lib, g, cin=0) == SHAPE
     assert conv(lib, g, dtype=2) == DTYPE
     assert conv(lib, g, ptrs=[A, None, A + 512 * MB, A + 768 * MB]) == NULL   # stale needed (n > 1)
