@@ -29,12 +29,15 @@
 //    a lane then holds 16 keys of ONE query per 32x32 block, so the row max and
 //    row sum are in-lane reductions plus one exchange between the two
 //    half-waves;
-//  * online softmax in the log2 domain (exp2(s*scale*log2e - m)) with the
-//    exact running max; O and l are rescaled only when some row of the wave
-//    saw a new max (a wave-uniform branch that long key loops mostly skip);
-//    the row sum l adds the bf16-rounded P (v_dot2_f32_bf16) so numerator and
-//    denominator carry the same rounding - a row dominated by one key then
-//    returns that key's V exactly;
+//  * online softmax in the log2 domain (exp2(s*scale*log2e - m)) with a lazy
+//    running max: the reference m moves (and O and l are rescaled, a
+//    wave-uniform branch) only when some row of the wave exceeds it by more
+//    than kLazy, so after the first tile long key loops almost never
+//    rescale.  P is then at most 2^kLazy, which bf16 and the fp32
+//    accumulators carry with the same relative precision.  The row sum l
+//    adds the bf16-rounded P (v_dot2_f32_bf16) so numerator and denominator
+//    carry the same rounding - a row dominated by one key then returns that
+//    key's V exactly;
 //  * P is rounded to bf16 and fed straight from the S^T accumulators into the
 //    PV MFMA as its B operand (the accumulator layout already matches the
 //    operand layout, with the V^T reads permuted to agree).
@@ -57,6 +60,7 @@ constexpr int QTILE = NWAVES * QB * 32;
 constexpr int KPITCH = D + 8;   // LDS row pitch of K (bf16 elements)
 constexpr int VPITCH = KT + 4;  // LDS row pitch of V^T (bf16 elements)
 constexpr int kPartialCost = 3; // cost of one partial write + merge, in key tiles
+constexpr float kLazy = 8.0f;   // log2-domain slack of the running max
 
 // Work plan shared by the host launcher and both kernels.
 struct Plan {
@@ -284,11 +288,12 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
             // the other half-wave holds the other 16 keys of each 32-key block
             const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                              false, false);
-            mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-            const float mnew = __builtin_fmaxf(m[qb], mx * a.c);
-            // exact running max; the rescale is skipped when no row of the
-            // wave saw a larger score (wave-uniform branch)
-            if (__any(mnew > m[qb])) {
+            mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.c;
+            // lazy running max: keep the reference m until some row of the
+            // wave exceeds it by more than kLazy (always on the first tile,
+            // where m = -inf); then rescale O and l (wave-uniform branch)
+            if (__any(mx > m[qb] + kLazy)) {
+                const float mnew = __builtin_fmaxf(m[qb], mx);
                 const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
                 l[qb] *= alpha;
 #pragma unroll
