@@ -11,7 +11,8 @@ of K, V, the conv input and the GroupNorm moments into the stale buffers.
 Inputs are seeded synthetic bf16 tensors already resident in HBM.
 
 Prints one JSON line.  `value` is (attention + conv FLOPs of both levels) /
-step time in TFLOP/s.  Per-op figures (attention and conv TFLOP/s, GroupNorm
+step time in TFLOP/s; the step is captured once in a HIP graph and the
+timed steps are graph replays (the eager step time is reported beside it).  Per-op figures (attention and conv TFLOP/s, GroupNorm
 and refresh GB/s with buffers rotated through > 512 MB so the 256 MB
 Infinity Cache cannot serve them) ride along, plus the roofline of the
 dominant kernel (attention at level a) and the CPU oracle's rate on a bounded
@@ -46,6 +47,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time budget of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time the step with eager launches only (default: also capture it in a "
+                         "HIP graph and take the replay time as the step time)")
     ap.add_argument("--profile-op", choices=["attn", "conv", "gn", "refresh", "copy"],
                     help="run only this op (--steps times) for counter collection, print nothing else")
     ap.add_argument("--level", default="sdxl3840_l2", choices=list(LEVELS))
@@ -389,7 +393,35 @@ def main():
     lb = sorted(e[1].elapsed_time(e[2]) for e in layer_ev)
     attn_ms = sum(a.elapsed_time(b) for a, b in attn_ev) / args.steps
 
+    # the same step captured once in a HIP graph and replayed: the launch
+    # gaps between the step's 20 kernels shrink to the graph's
+    graph_ms = None
+    if not args.no_graph:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for lv in levels:
+                lv.layer()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for lv in levels:
+                lv.layer()
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        del g
+
     flops = sum(lv.wl.attn_flops() + lv.wl.conv_flops() for lv in levels)
+    eager_ms = step_ms
+    if graph_ms is not None:
+        step_ms = graph_ms
     value = flops / (step_ms * 1e-3) / 1e12
     ops = per_op(levels, args.op_iters)
     copy = copy_peak(args.op_iters)
@@ -404,6 +436,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
+        "ms_per_step_eager": round(eager_ms, 4),
+        "step_launch": "hip graph replay" if graph_ms is not None else "eager",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -1,0 +1,88 @@
+"""The patch layer captured in a HIP graph (as bench.py times it) must give,
+on every replay, the same bits as the eager calls.  Between replays the test
+runs eager work of its own and synchronises, so a node that only behaves on
+the first replay shows up."""
+import pytest
+import torch
+
+import displaced_patch_parallelism_distri_amd as dp
+import synthetic_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    dp.load()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def test_layer_graph_replays_match_eager():
+    wl = si.WORKLOADS["sdxl1024_l2"].with_patch(3)
+    dev = torch.device("cuda:0")
+    d = si.make_inputs(wl, device=dev, nonzero_bias=True)
+    B, n, G = wl.batch, wl.n_patches, wl.groups
+    table0 = torch.rand(B, n, G, 2, device=dev) + torch.tensor([0.0, 1.0], device=dev)
+    gn_ws = torch.empty(dp.distri_async_groupnorm_workspace_size(wl.geom, wl.channels, G, dp.DISTRI_BF16),
+                        dtype=torch.uint8, device=dev)
+    at_ws = torch.empty(max(1, dp.distri_patch_self_attn_workspace_size(wl.geom, wl.heads, 64, dp.DISTRI_BF16)),
+                        dtype=torch.uint8, device=dev)
+    tok_row = wl.width * wl.heads * 64
+
+    def make_state():
+        return {"ks": d["k_stale"].clone(), "vs": d["v_stale"].clone(), "xs": d["x_stale"].clone(),
+                "table": table0.clone(), "y_gn": torch.empty_like(d["x_fresh"]),
+                "fm": torch.empty(B, G, 2, device=dev),
+                "y_conv": torch.empty_like(d["x_fresh"]), "out": torch.empty_like(d["q"])}
+
+    def layer(st):
+        dp.distri_async_groupnorm(wl.geom, G, d["x_fresh"], st["table"], d["gamma"], d["beta"],
+                                  y=st["y_gn"], fresh_moments=st["fm"], workspace=gn_ws)
+        dp.distri_patch_conv3x3_halo(wl.geom, st["y_gn"], st["xs"], d["weight"], d["bias"], y=st["y_conv"])
+        dp.distri_patch_self_attn(wl.geom, wl.heads, d["q"], d["k_fresh"], d["v_fresh"], st["ks"], st["vs"],
+                                  out=st["out"], workspace=at_ws)
+        dp.distri_refresh_stale(wl.geom, tok_row, d["k_fresh"], st["ks"])
+        dp.distri_refresh_stale(wl.geom, tok_row, d["v_fresh"], st["vs"])
+        dp.distri_refresh_stale(wl.geom, wl.width * wl.channels, st["y_gn"], st["xs"])
+        dp.distri_refresh_stale((B, n, 1, n, wl.patch), 2 * G, st["fm"], st["table"])
+
+    # eager reference: the first call (stale buffers as given) and a second
+    # call (stale buffers already refreshed)
+    ref = make_state()
+    layer(ref)
+    torch.cuda.synchronize()
+    first = {k: v.clone() for k, v in ref.items()}
+    layer(ref)
+    torch.cuda.synchronize()
+    second = {k: v.clone() for k, v in ref.items()}
+
+    st = make_state()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    warm = make_state()
+    with torch.cuda.stream(side):
+        layer(warm)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        layer(st)
+    # capture does not execute: reset the state, then replay
+    for k, v in make_state().items():
+        st[k].copy_(v)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        want = first if rep == 0 else second
+        for k in ("y_gn", "fm", "y_conv", "out", "ks", "vs", "xs", "table"):
+            assert torch.equal(_bits(st[k]), _bits(want[k])), f"replay {rep}: {k} differs from eager"
+        # eager work of the program's own between replays
+        junk = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
