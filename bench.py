@@ -356,7 +356,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU exchange is a design note, not part of this build)", file=sys.stderr)
+              "(the exchange between patch devices is not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
 

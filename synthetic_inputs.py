@@ -70,7 +70,8 @@ class Workload:
     def with_patch(self, i):
         return replace(self, patch=i)
 
-    # algorithmic work, counted as in the measurement section of the design
+    # algorithmic work: attention counts Q K^T and P V (not the softmax); the
+    # conv counts all 9 taps, zero-padded edge taps included
     def attn_flops(self):
         return 4.0 * self.batch * self.heads * self.lq * self.tokens * self.head_dim
 
