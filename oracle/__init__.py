@@ -45,8 +45,11 @@ def _load():
         lib.oracle_group_moments.argtypes = [_I] * 5 + [_D, _D]
         lib.oracle_async_groupnorm.argtypes = [_I] * 7 + [ctypes.c_double] + [_D] * 6
         lib.oracle_refresh_stale.argtypes = [_I] * 5 + [_D, _D]
+        lib.oracle_linear.argtypes = [_I] * 3 + [_D] * 4
+        lib.oracle_patch_qkv_proj.argtypes = [_I] * 6 + [_D] * 8
         for f in ("oracle_patch_self_attn", "oracle_patch_conv3x3_halo", "oracle_group_moments",
-                  "oracle_async_groupnorm", "oracle_refresh_stale"):
+                  "oracle_async_groupnorm", "oracle_refresh_stale", "oracle_linear",
+                  "oracle_patch_qkv_proj"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -141,3 +144,38 @@ def refresh_stale(geom, row_elems, fresh, stale):
     rc = _load().oracle_refresh_stale(B, H, n, i, row_elems, _p(f), _p(s))
     _check(rc, "refresh_stale")
     return s
+
+
+def linear(x, weight, bias=None):
+    """Token-wise linear map: x [..., C], weight [N, C], bias [N] or None ->
+    [..., N] float64 (y = x W^T + b)."""
+    xf = _f64(x)
+    w = _f64(weight)
+    b = _f64(bias)
+    C = xf.shape[-1]
+    N = w.shape[0]
+    M = xf.size // C if C else 0
+    y = np.zeros(xf.shape[:-1] + (N,), dtype=np.float64)
+    rc = _load().oracle_linear(M, C, N, _p(xf), _p(w), _p(b), _p(y))
+    _check(rc, "linear")
+    return y
+
+
+def patch_qkv_proj(geom, channels, x, w_qkv, bias=None, k_stale=None, v_stale=None):
+    """Q/K/V projection of patch i's hidden states x [B, h, W, C] with
+    w_qkv [3C, C] (Q, K, V weights stacked), bias [3C] or None.  Returns
+    (q, k, v) as [B, Lq, C] and, for each given stale map [B, H*W, C], a copy
+    with patch i's rows replaced by the new k / v (else None)."""
+    B, H, W, n, i = geom
+    C = channels
+    Lq = (H // n) * W
+    xf, w, b = _f64(x), _f64(w_qkv), _f64(bias)
+    q = np.zeros((B, Lq, C), dtype=np.float64)
+    k = np.zeros_like(q)
+    v = np.zeros_like(q)
+    ks = None if k_stale is None else _f64(k_stale).reshape(B, H * W, C).copy()
+    vs = None if v_stale is None else _f64(v_stale).reshape(B, H * W, C).copy()
+    rc = _load().oracle_patch_qkv_proj(B, H, W, n, i, C, _p(xf), _p(w), _p(b), _p(q), _p(k), _p(v),
+                                       _p(ks), _p(vs))
+    _check(rc, "patch_qkv_proj")
+    return q, k, v, ks, vs

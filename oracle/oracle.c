@@ -282,3 +282,65 @@ int oracle_refresh_stale(int64_t B, int64_t H, int64_t n, int64_t i, int64_t row
                 stale[(b * H + i * h + r) * row_elems + e] = fresh[(b * h + r) * row_elems + e];
     return 0;
 }
+
+/* Token-wise linear map, the form of the attention layer's Q/K/V and output
+ * projections (the modules that the wrapped self-attention holds: source
+ * walkthrough, section "Patch Parallelism的实现原理", item 2):
+ *   y[m, o] = bias[o] + sum_c w[o, c] * x[m, c]     m < M, o < N
+ * x [M, C], w [N, C] (row o holds output o's weights), bias [N] or NULL,
+ * y [M, N]. */
+int oracle_linear(int64_t M, int64_t C, int64_t N, const double *x, const double *w,
+                  const double *bias, double *y)
+{
+    if (M < 0 || C < 0 || N < 0)
+        return -1;
+    int64_t m;
+#pragma omp parallel for schedule(static)
+    for (m = 0; m < M; ++m) {
+        for (int64_t o = 0; o < N; ++o) {
+            double acc = bias ? bias[o] : 0.0;
+            for (int64_t c = 0; c < C; ++c)
+                acc += w[o * C + c] * x[m * C + c];
+            y[m * N + o] = acc;
+        }
+    }
+    return 0;
+}
+
+/* Q/K/V projection of patch i with the refresh folded in.  x [B, h, W, C]
+ * holds the patch's hidden states (token t = r * W + c of the patch);
+ * w_qkv [3C, C] stacks the Q, K and V weights, bias [3C] or NULL:
+ *   [q | k | v][b, t, :] = linear(x[b, t, :])       each [B, Lq, C]
+ * and, when k_stale / v_stale [B, H*W, C] are given, their rows of patch i
+ * take the new k / v (the previous step's stale maps then hold this step's
+ * fresh K/V for the next step, as a separate refresh would leave them). */
+int oracle_patch_qkv_proj(int64_t B, int64_t H, int64_t W, int64_t n, int64_t i, int64_t C,
+                          const double *x, const double *w_qkv, const double *bias, double *q,
+                          double *k, double *v, double *k_stale, double *v_stale)
+{
+    if (n <= 0 || H % n != 0 || i < 0 || i >= n || C <= 0)
+        return -1;
+    const int64_t Lq = (H / n) * W, L = H * W, M = B * Lq;
+    double *y = (double *)malloc(sizeof(double) * (size_t)(M * 3 * C));
+    if (!y)
+        return -2;
+    oracle_linear(M, C, 3 * C, x, w_qkv, bias, y);
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t c = 0; c < C; ++c) {
+            q[m * C + c] = y[m * 3 * C + c];
+            k[m * C + c] = y[m * 3 * C + C + c];
+            v[m * C + c] = y[m * 3 * C + 2 * C + c];
+        }
+    free(y);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t t = 0; t < Lq; ++t)
+            for (int64_t c = 0; c < C; ++c) {
+                const int64_t src = (b * Lq + t) * C + c;
+                const int64_t dst = (b * L + i * Lq + t) * C + c;
+                if (k_stale)
+                    k_stale[dst] = k[src];
+                if (v_stale)
+                    v_stale[dst] = v[src];
+            }
+    return 0;
+}
