@@ -19,7 +19,7 @@ __all__ = [
     "DistriError", "load", "abi_version", "geom",
     "distri_patch_self_attn", "distri_patch_conv3x3_halo", "distri_async_groupnorm",
     "distri_refresh_stale", "distri_patch_self_attn_workspace_size",
-    "distri_async_groupnorm_workspace_size",
+    "distri_async_groupnorm_workspace_size", "distri_patch_qkv_proj", "distri_patch_out_proj",
     "DISTRI_F32", "DISTRI_BF16",
 ]
 
@@ -32,7 +32,8 @@ STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN"
 SYMBOLS = ("distri_abi_version", "distri_status_str", "distri_last_error",
            "distri_patch_self_attn_workspace_size", "distri_patch_self_attn",
            "distri_patch_conv3x3_halo", "distri_async_groupnorm_workspace_size",
-           "distri_async_groupnorm", "distri_refresh_stale")
+           "distri_async_groupnorm", "distri_refresh_stale", "distri_patch_qkv_proj",
+           "distri_patch_out_proj")
 
 
 class DistriError(RuntimeError):
@@ -70,6 +71,8 @@ def load():
     lib.distri_async_groupnorm_workspace_size.argtypes = [G, I64, I64, I, ctypes.POINTER(SZ)]
     lib.distri_async_groupnorm.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 7 + [SZ, P]
     lib.distri_refresh_stale.argtypes = [G, I64, I, P, P, P]
+    lib.distri_patch_qkv_proj.argtypes = [G, I64, I] + [P] * 9
+    lib.distri_patch_out_proj.argtypes = [G, I64, I] + [P] * 5
     for name in SYMBOLS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -232,3 +235,45 @@ def distri_refresh_stale(g, row_elems, fresh, stale, stream=None):
         _ptr(stale, "stale", fresh.dtype, g.batch * g.height * row_elems), _stream(stream))
     _check(st, "distri_refresh_stale")
     return stale
+
+
+def distri_patch_qkv_proj(g, x, w_qkv, bias=None, q=None, k_fresh=None, v_fresh=None, k_stale=None,
+                          v_stale=None, stream=None):
+    """Q/K/V projection of patch i: x [B, h, W, C] (or [B, Lq, C]), w_qkv
+    [3C, C], bias [3C] fp32 or None -> (q, k_fresh, v_fresh), each [B, Lq, C];
+    k_stale / v_stale [B, H*W, C] (optional) get patch i's rows of k / v."""
+    g = _as_geom(g)
+    code = _dtype_code(x)
+    C = x.shape[-1]
+    lq = (g.height // max(g.n_patches, 1)) * g.width
+    shape = (g.batch, lq, C)
+    q = torch.empty(shape, dtype=x.dtype, device=x.device) if q is None else q
+    k_fresh = torch.empty(shape, dtype=x.dtype, device=x.device) if k_fresh is None else k_fresh
+    v_fresh = torch.empty(shape, dtype=x.dtype, device=x.device) if v_fresh is None else v_fresh
+    n_tok = g.batch * lq * C
+    n_full = g.batch * g.height * g.width * C
+    st = load().distri_patch_qkv_proj(
+        ctypes.byref(g), C, code, _ptr(x, "x", x.dtype, n_tok), _ptr(w_qkv, "w_qkv", x.dtype, 3 * C * C),
+        _ptr(bias, "bias", torch.float32, 3 * C), _ptr(q, "q", x.dtype, n_tok),
+        _ptr(k_fresh, "k_fresh", x.dtype, n_tok), _ptr(v_fresh, "v_fresh", x.dtype, n_tok),
+        _ptr(k_stale, "k_stale", x.dtype, n_full), _ptr(v_stale, "v_stale", x.dtype, n_full),
+        _stream(stream))
+    _check(st, "distri_patch_qkv_proj")
+    return q, k_fresh, v_fresh
+
+
+def distri_patch_out_proj(g, o, w_o, bias=None, y=None, stream=None):
+    """Output projection of patch i: o [B, Lq, C] (or [B, Lq, heads, d]),
+    w_o [C, C], bias [C] fp32 or None -> y [B, Lq, C]."""
+    g = _as_geom(g)
+    code = _dtype_code(o)
+    C = w_o.shape[0]
+    lq = (g.height // max(g.n_patches, 1)) * g.width
+    if y is None:
+        y = torch.empty((g.batch, lq, C), dtype=o.dtype, device=o.device)
+    n_tok = g.batch * lq * C
+    st = load().distri_patch_out_proj(
+        ctypes.byref(g), C, code, _ptr(o, "o", o.dtype, n_tok), _ptr(w_o, "w_o", o.dtype, C * C),
+        _ptr(bias, "bias", torch.float32, C), _ptr(y, "y", o.dtype, n_tok), _stream(stream))
+    _check(st, "distri_patch_out_proj")
+    return y

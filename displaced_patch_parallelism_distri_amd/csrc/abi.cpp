@@ -292,4 +292,73 @@ int distri_refresh_stale(const distri_patch_geom* g, int64_t row_elems, int dtyp
                                          static_cast<hipStream_t>(stream)));
 }
 
+
+int distri_patch_qkv_proj(const distri_patch_geom* g, int64_t channels, int dtype, const void* x,
+                          const void* w_qkv, const float* bias, void* q, void* k_fresh,
+                          void* v_fresh, void* k_stale, void* v_stale, void* stream) {
+    int st = check_geom(g);
+    if (st) return st;
+    st = check_dtype(dtype);
+    if (st) return st;
+    DP_CHECK(channels >= 1, DISTRI_ERR_SHAPE, "channels must be >= 1");
+    DP_CHECK(channels <= 65536, DISTRI_ERR_UNSUPPORTED, "channels above 65536");
+    if (dtype == DISTRI_BF16)
+        DP_CHECK(channels % 64 == 0, DISTRI_ERR_UNSUPPORTED, "bf16 projections need channels % 64 == 0");
+    const dp::Geom gg = to_geom(g);
+    DP_CHECK(gg.B * gg.lq() < (int64_t(1) << 31), DISTRI_ERR_UNSUPPORTED,
+             "batch * patch tokens must stay below 2^31");
+    DP_CHECK(dp::proj_launch_fits(gg.B * gg.lq(), 3 * channels), DISTRI_ERR_UNSUPPORTED,
+             "projection output too large for one launch");
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t tok = size_t(gg.B * gg.lq() * channels) * eb;
+    if (tok == 0) return DISTRI_OK;
+    DP_CHECK(x && w_qkv && q && k_fresh && v_fresh, DISTRI_ERR_NULL, "a tensor pointer is NULL");
+    DP_CHECK(aligned16(x) && aligned16(w_qkv) && aligned16(bias) && aligned16(q) &&
+                 aligned16(k_fresh) && aligned16(v_fresh) && aligned16(k_stale) && aligned16(v_stale),
+             DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const size_t full = size_t(gg.B * gg.L() * channels) * eb;
+    const Range ins[3] = {{x, tok}, {w_qkv, size_t(3 * channels * channels) * eb},
+                          {bias, bias ? size_t(3 * channels) * 4 : 0}};
+    const Range outs[5] = {{q, tok}, {k_fresh, tok}, {v_fresh, tok}, {k_stale, k_stale ? full : 0},
+                           {v_stale, v_stale ? full : 0}};
+    for (const Range& o : outs)
+        for (const Range& in : ins)
+            DP_CHECK(!overlaps(o, in), DISTRI_ERR_ALIAS, "an output overlaps an input");
+    for (int a = 0; a < 5; ++a)
+        for (int b = a + 1; b < 5; ++b)
+            DP_CHECK(!overlaps(outs[a], outs[b]), DISTRI_ERR_ALIAS, "outputs overlap each other");
+    return hip_status(dp::launch_qkv_proj(gg, channels, dtype == DISTRI_BF16, x, w_qkv, bias, q,
+                                          k_fresh, v_fresh, k_stale, v_stale,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int distri_patch_out_proj(const distri_patch_geom* g, int64_t channels, int dtype, const void* o,
+                          const void* w_o, const float* bias, void* y, void* stream) {
+    int st = check_geom(g);
+    if (st) return st;
+    st = check_dtype(dtype);
+    if (st) return st;
+    DP_CHECK(channels >= 1, DISTRI_ERR_SHAPE, "channels must be >= 1");
+    DP_CHECK(channels <= 65536, DISTRI_ERR_UNSUPPORTED, "channels above 65536");
+    if (dtype == DISTRI_BF16)
+        DP_CHECK(channels % 64 == 0, DISTRI_ERR_UNSUPPORTED, "bf16 projections need channels % 64 == 0");
+    const dp::Geom gg = to_geom(g);
+    DP_CHECK(gg.B * gg.lq() < (int64_t(1) << 31), DISTRI_ERR_UNSUPPORTED,
+             "batch * patch tokens must stay below 2^31");
+    DP_CHECK(dp::proj_launch_fits(gg.B * gg.lq(), channels), DISTRI_ERR_UNSUPPORTED,
+             "projection output too large for one launch");
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t tok = size_t(gg.B * gg.lq() * channels) * eb;
+    if (tok == 0) return DISTRI_OK;
+    DP_CHECK(o && w_o && y, DISTRI_ERR_NULL, "a tensor pointer is NULL");
+    DP_CHECK(aligned16(o) && aligned16(w_o) && aligned16(bias) && aligned16(y), DISTRI_ERR_ALIGN,
+             "tensor pointers must be 16-byte aligned");
+    const Range out{y, tok};
+    DP_CHECK(!overlaps(out, {o, tok}) && !overlaps(out, {w_o, size_t(channels * channels) * eb}) &&
+                 !overlaps(out, {bias, bias ? size_t(channels) * 4 : 0}),
+             DISTRI_ERR_ALIAS, "y overlaps an input");
+    return hip_status(dp::launch_out_proj(gg, channels, dtype == DISTRI_BF16, o, w_o, bias, y,
+                                          static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

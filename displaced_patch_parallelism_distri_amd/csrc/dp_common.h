@@ -98,6 +98,14 @@ hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16
                             const void* kf, const void* vf, const void* ks, const void* vs,
                             void* out, void* ws, hipStream_t s);
 
+hipError_t launch_qkv_proj(const Geom& g, int64_t C, bool bf16, const void* x, const void* w_qkv,
+                           const float* bias, void* q, void* k, void* v, void* k_stale,
+                           void* v_stale, hipStream_t s);
+hipError_t launch_out_proj(const Geom& g, int64_t C, bool bf16, const void* o, const void* w_o,
+                           const float* bias, void* y, hipStream_t s);
+// whether an M x N projection output fits one launch's grid
+bool proj_launch_fits(int64_t M, int64_t N);
+
 hipError_t launch_conv3x3(const Geom& g, int64_t cin, int64_t cout, bool bf16, const void* xf,
                           const void* xs, const void* w, const float* bias, void* y,
                           hipStream_t s);

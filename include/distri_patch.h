@@ -175,6 +175,45 @@ int distri_async_groupnorm(const distri_patch_geom *g, int64_t channels, int64_t
 int distri_refresh_stale(const distri_patch_geom *g, int64_t row_elems, int dtype,
                          const void *fresh, void *stale, void *stream);
 
+/*
+ * distri_patch_qkv_proj - Q/K/V projection of patch i's hidden states (the
+ * projections that the wrapped self-attention holds: source walkthrough,
+ * section "Patch Parallelism的实现原理", item 2), with the refresh of the
+ * stale K/V maps folded in.  For every image b and patch token t:
+ *   [q | k | v][b, t, :] = bias + w_qkv * x[b, t, :]      (each [C] of [3C])
+ * and, when k_stale / v_stale are given, their rows of patch i take the new
+ * values (k_stale[b, i*Lq + t, :] = k[b, t, :], likewise v): this step's
+ * fresh K/V become the next step's stale context (README mirror, section
+ * 概述, figure (c)) without a separate distri_refresh_stale.  Attention never
+ * reads the stale maps' own rows, so they may be written before it runs.
+ *
+ *   x                   [B, h, W, C] = [B, Lq, C]   dtype (token-major)
+ *   w_qkv               [3C, C] dtype: rows 0..C-1 Q, C..2C-1 K, 2C..3C-1 V
+ *   bias                [3C] fp32 or NULL
+ *   q, k_fresh, v_fresh [B, Lq, C] dtype (outputs; [B, Lq, heads, 64] for
+ *                       distri_patch_self_attn when C = heads * 64)
+ *   k_stale, v_stale    [B, H*W, C] dtype or NULL (rows of patch i written)
+ * bf16 requires C % 64 == 0; C <= 65536 and B*Lq < 2^31
+ * (DISTRI_ERR_UNSUPPORTED).  bf16 inputs use bf16 MFMA with fp32
+ * accumulation; each output is rounded to bf16 once and the stale copy holds
+ * the same bits.
+ */
+int distri_patch_qkv_proj(const distri_patch_geom *g, int64_t channels, int dtype,
+                          const void *x, const void *w_qkv, const float *bias, void *q,
+                          void *k_fresh, void *v_fresh, void *k_stale, void *v_stale,
+                          void *stream);
+
+/*
+ * distri_patch_out_proj - output projection of the patch's attention result
+ * (same module as above):
+ *   y[b, t, :] = bias + w_o * o[b, t, :]
+ *   o, y   [B, Lq, C] dtype      w_o  [C, C] dtype      bias [C] fp32 or NULL
+ * Same limits as distri_patch_qkv_proj.
+ */
+int distri_patch_out_proj(const distri_patch_geom *g, int64_t channels, int dtype,
+                          const void *o, const void *w_o, const float *bias, void *y,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -149,3 +149,36 @@ def make_map(shape, seed, dtype=torch.float32, device="cpu", scale=1.0):
     g = torch.Generator(device=device)
     g.manual_seed(seed)
     return (scale * torch.randn(*shape, generator=g, device=device, dtype=torch.float32)).to(dtype)
+
+
+def make_proj_inputs(wl: Workload, device="cpu"):
+    """Seeded inputs of the attention layer's projections for patch
+    ``wl.patch`` (their own generator, seeded with ``seed + 7919``, so the
+    tensors of ``make_inputs`` are unchanged).  Drawn in this order:
+      1. x      [B, Lq, C]   ~ N(0, 1)     hidden states of the patch's tokens
+      2. w_qkv  [3C, C]      ~ N(0, 1 / C) Q, K, V weights stacked by rows
+      3. b_qkv  [3C] fp32    = 0.1 N(0, 1)
+      4. o      [B, Lq, C]   ~ N(0, 1)     attention output of the patch
+      5. w_o    [C, C]       ~ N(0, 1 / C)
+      6. b_o    [C] fp32     = 0.1 N(0, 1)
+      7. k_stale, v_stale [B, H*W, C] ~ N(0, 1)  last step's K / V maps
+    Rounded to the workload dtype (biases stay fp32)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed + 7919)
+    B, C, L, Lq = wl.batch, wl.channels, wl.tokens, wl.lq
+    dt = wl.torch_dtype
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+
+    out = {
+        "x": randn(B, Lq, C).to(dt),
+        "w_qkv": (randn(3 * C, C) * C ** -0.5).to(dt),
+        "b_qkv": 0.1 * randn(3 * C),
+        "o": randn(B, Lq, C).to(dt),
+        "w_o": (randn(C, C) * C ** -0.5).to(dt),
+        "b_o": 0.1 * randn(C),
+    }
+    out["k_stale"] = randn(B, L, C).to(dt)
+    out["v_stale"] = randn(B, L, C).to(dt)
+    return {k: v.contiguous() for k, v in out.items()}

@@ -149,3 +149,54 @@ def test_python_binding_raises_on_cpu_tensors():
     x = torch.zeros(2, 8, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         dp.distri_refresh_stale((2, 32, 8, 4, 0), 8 * 64, x, torch.zeros(2, 32, 8, 64, dtype=torch.bfloat16))
+
+
+def qkv(lib, geom, C=640, dtype=BF16, ptrs=None, bias=None):
+    p = ptrs or [A + k * 512 * MB for k in range(7)]
+    x, w, q, k, v, ks, vs = p
+    return lib.distri_patch_qkv_proj(G(*geom), C, dtype, x, w, bias, q, k, v, ks, vs, None)
+
+
+def test_qkv_proj_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    assert qkv(lib, (2, 240, 240, 8, 8)) == SHAPE
+    assert qkv(lib, g, C=0) == SHAPE
+    assert qkv(lib, g, C=96) == UNSUP                    # bf16 needs C % 64 == 0
+    assert qkv(lib, g, C=65600) == UNSUP
+    assert qkv(lib, g, dtype=3) == DTYPE
+    assert qkv(lib, (70000, 240, 240, 8, 4)) == UNSUP    # B * Lq >= 2^31
+    assert qkv(lib, (1, 1 << 22, 4096, 1024, 0), C=65536) == UNSUP  # grid too large
+    p = [A + k * 512 * MB for k in range(7)]
+    p[1] = None
+    assert qkv(lib, g, ptrs=p) == NULL
+    p = [A + k * 512 * MB for k in range(7)]
+    p[4] += 8
+    assert qkv(lib, g, ptrs=p) == ALIGN
+    assert qkv(lib, g, bias=A + 7 * 512 * MB + 4) == ALIGN
+    p = [A + k * 512 * MB for k in range(7)]
+    p[3] = p[0] + 1024                                   # k inside x
+    assert qkv(lib, g, ptrs=p) == ALIAS
+    p = [A + k * 512 * MB for k in range(7)]
+    p[6] = p[5] + 1024                                   # the two stale maps overlap
+    assert qkv(lib, g, ptrs=p) == ALIAS
+    p = [A + k * 512 * MB for k in range(7)]
+    assert qkv(lib, g, bias=p[2] + 64) == ALIAS          # q written over the bias
+    assert qkv(lib, (0, 240, 240, 8, 4), ptrs=[None] * 7) == OK
+
+
+def test_out_proj_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    o, w, y = A, A + 512 * MB, A + 1024 * MB
+
+    def call(geom=g, C=640, dtype=BF16, o=o, w=w, bias=None, y=y):
+        return lib.distri_patch_out_proj(G(*geom), C, dtype, o, w, bias, y, None)
+
+    assert call(C=-1) == SHAPE
+    assert call(C=32) == UNSUP
+    assert call(dtype=9) == DTYPE
+    assert call(o=None) == NULL
+    assert call(y=y + 2) == ALIGN
+    assert call(y=o + 4096) == ALIAS
+    assert call(bias=y + 256) == ALIAS
+    assert call(geom=(2, 241, 240, 8, 4)) == SHAPE
+    assert call(geom=(2, 240, 0, 8, 4), o=None, w=None, y=None) == OK
