@@ -47,9 +47,10 @@ def _load():
         lib.oracle_refresh_stale.argtypes = [_I] * 5 + [_D, _D]
         lib.oracle_linear.argtypes = [_I] * 3 + [_D] * 4
         lib.oracle_patch_qkv_proj.argtypes = [_I] * 6 + [_D] * 8
+        lib.oracle_silu.argtypes = [_I, _D, _D]
         for f in ("oracle_patch_self_attn", "oracle_patch_conv3x3_halo", "oracle_group_moments",
                   "oracle_async_groupnorm", "oracle_refresh_stale", "oracle_linear",
-                  "oracle_patch_qkv_proj"):
+                  "oracle_patch_qkv_proj", "oracle_silu"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -179,3 +180,104 @@ def patch_qkv_proj(geom, channels, x, w_qkv, bias=None, k_stale=None, v_stale=No
                                        _p(ks), _p(vs))
     _check(rc, "patch_qkv_proj")
     return q, k, v, ks, vs
+
+
+def silu(z):
+    """Elementwise z / (1 + exp(-z)), float64, same shape."""
+    zf = _f64(z)
+    y = np.zeros_like(zf)
+    _check(_load().oracle_silu(zf.size, _p(zf), _p(y)), "silu")
+    return y
+
+
+# ---------------------------------------------------------------- patch block
+# The wrapped layers chained at patch granularity for one denoising step
+# ("DistriFusion源码探秘", section "Patch Parallelism的实现原理": conv,
+# self-attention and GroupNorm are the wrapped layer types):
+#   g1 = SiLU(GN1(x)); h = conv3x3(g1) + b; n2 = GN2(h);
+#   q, k, v = n2 Wqkv^T + b; o = softmax(scale q K^T) V; y = o Wo^T + b.
+# ``wts`` is a dict: channels, groups, heads, eps, scale, gn1_gamma, gn1_beta,
+# conv_w [C,3,3,C], conv_b, gn2_gamma, gn2_beta, w_qkv [3C,C], b_qkv, w_o
+# [C,C], b_o.  A state is a dict of the previous step's context: gn1, gn2
+# [B, n, G, 2] moment tables, conv_in [B, H, W, C] (g1 of every patch), k, v
+# [B, H*W, C].  These functions only sequence the C routines above.
+
+def patch_block(geom, wts, x, state):
+    """One asynchronous step for patch i: x [B, h, W, C] -> (y [B, Lq, C],
+    new state).  Stale reads come from ``state``; the new state is a copy
+    with patch i's rows / slots replaced by this step's fresh values (README
+    mirror, section 概述, figure (c): the next step reuses them)."""
+    B, H, W, n, i = geom
+    C, G, nh = wts["channels"], wts["groups"], wts["heads"]
+    h, Lq, L, d = H // n, (H // n) * W, H * W, C // nh
+    z1, fm1 = async_groupnorm(geom, C, G, wts["eps"], x, state["gn1"], wts["gn1_gamma"],
+                              wts["gn1_beta"])
+    g1 = silu(z1)
+    hh = patch_conv3x3_halo(geom, C, C, g1, state["conv_in"], wts["conv_w"], wts["conv_b"])
+    n2, fm2 = async_groupnorm(geom, C, G, wts["eps"], hh, state["gn2"], wts["gn2_gamma"],
+                              wts["gn2_beta"])
+    q, k, v, ks, vs = patch_qkv_proj(geom, C, n2, wts["w_qkv"], wts["b_qkv"], state["k"], state["v"])
+    o = patch_self_attn(geom, nh, d, wts["scale"], q.reshape(B, Lq, nh, d), k.reshape(B, Lq, nh, d),
+                        v.reshape(B, Lq, nh, d), _f64(state["k"]).reshape(B, L, nh, d),
+                        _f64(state["v"]).reshape(B, L, nh, d))
+    y = linear(o.reshape(B, Lq, C), wts["w_o"], wts["b_o"])
+    tgeom = (B, n, 1, n, i)
+    new = {
+        "gn1": refresh_stale(tgeom, 2 * G, fm1.reshape(B, 1, 2 * G),
+                             _f64(state["gn1"]).reshape(B, n, 2 * G)).reshape(B, n, G, 2),
+        "conv_in": refresh_stale(geom, W * C, g1.reshape(B, h, W * C),
+                                 _f64(state["conv_in"]).reshape(B, H, W * C)).reshape(B, H, W, C),
+        "gn2": refresh_stale(tgeom, 2 * G, fm2.reshape(B, 1, 2 * G),
+                             _f64(state["gn2"]).reshape(B, n, 2 * G)).reshape(B, n, G, 2),
+        "k": ks,
+        "v": vs,
+    }
+    return y, new
+
+
+def patch_block_sync(geom, wts, x_full):
+    """The synchronous (warm-up) step for all n patches: each stage runs for
+    every patch, and its fresh values are shared, before any patch reads
+    them in the next stage (the first denoising steps exchange activations
+    synchronously: README mirror, section 概述, figure (c)).
+    x_full [B, H, W, C] -> (y [B, H*W, C], state of this step)."""
+    B, H, W, n, _ = geom
+    C, G, nh = wts["channels"], wts["groups"], wts["heads"]
+    h, Lq, L, d = H // n, (H // n) * W, H * W, C // nh
+    xf = _f64(x_full)
+    geoms = [(B, H, W, n, j) for j in range(n)]
+    rows = [slice(j * h, (j + 1) * h) for j in range(n)]
+    toks = [slice(j * Lq, (j + 1) * Lq) for j in range(n)]
+    eps = wts["eps"]
+
+    gn1 = np.zeros((B, n, G, 2))
+    for j in range(n):
+        gn1[:, j] = group_moments(xf[:, rows[j]], G)
+    g1 = [silu(async_groupnorm(geoms[j], C, G, eps, xf[:, rows[j]], gn1, wts["gn1_gamma"],
+                               wts["gn1_beta"])[0]) for j in range(n)]
+    conv_in = np.zeros((B, H * W * C))
+    for j in range(n):
+        conv_in = refresh_stale(geoms[j], W * C, g1[j].reshape(B, h, W * C),
+                                conv_in.reshape(B, H, W * C))
+    conv_in = conv_in.reshape(B, H, W, C)
+    hh = [patch_conv3x3_halo(geoms[j], C, C, g1[j], conv_in, wts["conv_w"], wts["conv_b"])
+          for j in range(n)]
+    gn2 = np.zeros((B, n, G, 2))
+    for j in range(n):
+        gn2[:, j] = group_moments(hh[j], G)
+    n2 = [async_groupnorm(geoms[j], C, G, eps, hh[j], gn2, wts["gn2_gamma"], wts["gn2_beta"])[0]
+          for j in range(n)]
+    kmap = np.zeros((B, L, C))
+    vmap = np.zeros((B, L, C))
+    qkv = []
+    for j in range(n):
+        q, k, v, kmap, vmap = patch_qkv_proj(geoms[j], C, n2[j], wts["w_qkv"], wts["b_qkv"], kmap, vmap)
+        qkv.append((q, k, v))
+    y = np.zeros((B, L, C))
+    for j in range(n):
+        q, k, v = (t.reshape(B, Lq, nh, d) for t in qkv[j])
+        o = patch_self_attn(geoms[j], nh, d, wts["scale"], q, k, v, kmap.reshape(B, L, nh, d),
+                            vmap.reshape(B, L, nh, d))
+        y[:, toks[j]] = linear(o.reshape(B, Lq, C), wts["w_o"], wts["b_o"])
+    state = {"gn1": gn1, "conv_in": conv_in, "gn2": gn2, "k": kmap, "v": vmap}
+    return y, state

@@ -344,3 +344,12 @@ int oracle_patch_qkv_proj(int64_t B, int64_t H, int64_t W, int64_t n, int64_t i,
             }
     return 0;
 }
+
+/* SiLU, the activation that follows GroupNorm in SDXL's ResNet blocks:
+ * y = z * sigmoid(z) = z / (1 + exp(-z)), elementwise over n values. */
+int oracle_silu(int64_t n, const double *z, double *y)
+{
+    if (n < 0) return -1;
+    for (int64_t k = 0; k < n; ++k) y[k] = z[k] / (1.0 + exp(-z[k]));
+    return 0;
+}

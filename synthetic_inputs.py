@@ -182,3 +182,65 @@ def make_proj_inputs(wl: Workload, device="cpu"):
     out["k_stale"] = randn(B, L, C).to(dt)
     out["v_stale"] = randn(B, L, C).to(dt)
     return {k: v.contiguous() for k, v in out.items()}
+
+
+def make_block_inputs(wl: Workload, device="cpu"):
+    """Seeded inputs of the patch block (GroupNorm + SiLU -> conv ->
+    GroupNorm -> Q/K/V projection -> attention -> output projection) at the
+    shapes of ``wl`` (C = heads * head_dim); own generator, seeded with
+    ``seed + 104729``.  Drawn in this order:
+      1. x      [B, H, W, C]  ~ N(0, 1)    this step's full input map
+      2. x_prev [B, H, W, C]  = x + sigma N(0, 1)   the previous step's
+      3. conv_w [C, 3, 3, C]  ~ N(0, 1 / (9 C)),  conv_b = 0.1 N(0, 1)
+      4. gn1_gamma = 1 + 0.1 N, gn1_beta = 0.1 N, then gn2_gamma, gn2_beta
+      5. w_qkv [3C, C] ~ N(0, 1 / C), b_qkv = 0.1 N;  w_o [C, C], b_o likewise
+      6. a random previous-step state: conv_in [B, H, W, C] ~ N(0, 1);
+         k, v [B, H*W, C] ~ N(0, 1); moment tables gn1, gn2 [B, n, G, 2]
+         with first moment 0.1 N(0, 1) and second moment first^2 + U(0.5, 1.5)
+    Tensors in the workload dtype; biases, gammas, betas and tables fp32."""
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed + 104729)
+    B, H, W, C, n, G = wl.batch, wl.height, wl.width, wl.channels, wl.n_patches, wl.groups
+    L = H * W
+    dt = wl.torch_dtype
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32)
+
+    def table():
+        m1 = 0.1 * randn(B, n, G)
+        m2 = m1 * m1 + 0.5 + torch.rand(B, n, G, generator=g, device=device)
+        return torch.stack([m1, m2], dim=-1).contiguous()
+
+    x = randn(B, H, W, C)
+    x_prev = x + wl.sigma * randn(B, H, W, C)
+    wts = {
+        "conv_w": (randn(C, 3, 3, C) * (1.0 / (9.0 * C)) ** 0.5).to(dt),
+        "conv_b": 0.1 * randn(C),
+        "gn1_gamma": 1.0 + 0.1 * randn(C),
+        "gn1_beta": 0.1 * randn(C),
+        "gn2_gamma": 1.0 + 0.1 * randn(C),
+        "gn2_beta": 0.1 * randn(C),
+        "w_qkv": (randn(3 * C, C) * C ** -0.5).to(dt),
+        "b_qkv": 0.1 * randn(3 * C),
+        "w_o": (randn(C, C) * C ** -0.5).to(dt),
+        "b_o": 0.1 * randn(C),
+    }
+    state = {
+        "conv_in": randn(B, H, W, C).to(dt),
+        "k": randn(B, L, C).to(dt),
+        "v": randn(B, L, C).to(dt),
+        "gn1": table(),
+        "gn2": table(),
+    }
+    out = {"x": x.to(dt), "x_prev": x_prev.to(dt), "weights": wts, "state": state}
+    for d in (wts, state):
+        for k in d:
+            d[k] = d[k].contiguous()
+    return out
+
+
+def block_scalars(wl: Workload):
+    """The block's non-tensor parameters at the shapes of ``wl``."""
+    return {"channels": wl.channels, "groups": wl.groups, "heads": wl.heads, "eps": wl.eps,
+            "scale": wl.head_dim ** -0.5}
