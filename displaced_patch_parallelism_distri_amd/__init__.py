@@ -20,6 +20,9 @@ __all__ = [
     "distri_patch_self_attn", "distri_patch_conv3x3_halo", "distri_async_groupnorm",
     "distri_refresh_stale", "distri_patch_self_attn_workspace_size",
     "distri_async_groupnorm_workspace_size", "distri_patch_qkv_proj", "distri_patch_out_proj",
+    "distri_async_groupnorm_silu", "distri_group_moments", "distri_patch_block",
+    "distri_patch_block_sync", "distri_patch_block_workspace_size",
+    "distri_patch_block_sync_workspace_size", "BlockWeights", "BlockState",
     "DISTRI_F32", "DISTRI_BF16",
 ]
 
@@ -33,7 +36,9 @@ SYMBOLS = ("distri_abi_version", "distri_status_str", "distri_last_error",
            "distri_patch_self_attn_workspace_size", "distri_patch_self_attn",
            "distri_patch_conv3x3_halo", "distri_async_groupnorm_workspace_size",
            "distri_async_groupnorm", "distri_refresh_stale", "distri_patch_qkv_proj",
-           "distri_patch_out_proj")
+           "distri_patch_out_proj", "distri_async_groupnorm_silu", "distri_group_moments",
+           "distri_patch_block_workspace_size", "distri_patch_block",
+           "distri_patch_block_sync_workspace_size", "distri_patch_block_sync")
 
 
 class DistriError(RuntimeError):
@@ -45,6 +50,19 @@ class DistriError(RuntimeError):
 class Geom(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("height", ctypes.c_int64), ("width", ctypes.c_int64),
                 ("n_patches", ctypes.c_int64), ("patch", ctypes.c_int64)]
+
+
+class BlockWeights(ctypes.Structure):
+    """distri_block_weights: the block's sizes and weight pointers."""
+    _fields_ = [("channels", ctypes.c_int64), ("groups", ctypes.c_int64), ("heads", ctypes.c_int64),
+                ("eps", ctypes.c_float), ("scale", ctypes.c_float)] + [
+        (name, ctypes.c_void_p) for name in ("gn1_gamma", "gn1_beta", "conv_w", "conv_b", "gn2_gamma",
+                                             "gn2_beta", "w_qkv", "b_qkv", "w_o", "b_o")]
+
+
+class BlockState(ctypes.Structure):
+    """distri_block_state: the stale context maps of one block."""
+    _fields_ = [(name, ctypes.c_void_p) for name in ("gn1", "conv_in", "gn2", "k", "v")]
 
 
 _lib = None
@@ -73,6 +91,13 @@ def load():
     lib.distri_refresh_stale.argtypes = [G, I64, I, P, P, P]
     lib.distri_patch_qkv_proj.argtypes = [G, I64, I] + [P] * 9
     lib.distri_patch_out_proj.argtypes = [G, I64, I] + [P] * 5
+    lib.distri_async_groupnorm_silu.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 7 + [SZ, P]
+    lib.distri_group_moments.argtypes = [G, I64, I64, I, P, P, P, SZ, P]
+    BW, BS = ctypes.POINTER(BlockWeights), ctypes.POINTER(BlockState)
+    lib.distri_patch_block_workspace_size.argtypes = [G, BW, I, ctypes.POINTER(SZ)]
+    lib.distri_patch_block_sync_workspace_size.argtypes = [G, BW, I, ctypes.POINTER(SZ)]
+    lib.distri_patch_block.argtypes = [G, BW, I, P, P, BS, BS, P, SZ, P]
+    lib.distri_patch_block_sync.argtypes = [G, BW, I, P, P, BS, P, SZ, P]
     for name in SYMBOLS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -204,6 +229,35 @@ def distri_async_groupnorm(g, groups, x_fresh, stale_moments, gamma=None, beta=N
                            y=None, fresh_moments=None, workspace=None, stream=None):
     """Corrected async GroupNorm of patch i: x_fresh [B,h,W,C], stale_moments
     [B,n,G,2] fp32 -> (y [B,h,W,C], fresh_moments [B,G,2] fp32)."""
+    return _groupnorm("distri_async_groupnorm", g, groups, x_fresh, stale_moments, gamma, beta,
+                      eps, y, fresh_moments, workspace, stream)
+
+
+def distri_async_groupnorm_silu(g, groups, x_fresh, stale_moments, gamma=None, beta=None,
+                                eps=1e-5, y=None, fresh_moments=None, workspace=None, stream=None):
+    """distri_async_groupnorm followed by SiLU (same arguments and results)."""
+    return _groupnorm("distri_async_groupnorm_silu", g, groups, x_fresh, stale_moments, gamma,
+                      beta, eps, y, fresh_moments, workspace, stream)
+
+
+def distri_group_moments(g, groups, x_fresh, table, workspace=None, stream=None):
+    """table[:, i] = raw moments (E[x], E[x^2]) of patch i's x_fresh [B,h,W,C];
+    table [B,n,G,2] fp32 is updated in place and returned."""
+    g = _as_geom(g)
+    code = _dtype_code(x_fresh)
+    C = x_fresh.shape[-1]
+    ws_bytes = distri_async_groupnorm_workspace_size(g, C, groups, code)
+    ws, ws_len = _workspace(ws_bytes, x_fresh, workspace)
+    st = load().distri_group_moments(
+        ctypes.byref(g), C, groups, code, _ptr(x_fresh, "x_fresh", x_fresh.dtype),
+        _ptr(table, "table", torch.float32, g.batch * g.n_patches * groups * 2),
+        _ptr(ws, "workspace"), ws_len, _stream(stream))
+    _check(st, "distri_group_moments")
+    return table
+
+
+def _groupnorm(func, g, groups, x_fresh, stale_moments, gamma, beta, eps, y, fresh_moments,
+               workspace, stream):
     g = _as_geom(g)
     code = _dtype_code(x_fresh)
     C = x_fresh.shape[-1]
@@ -213,14 +267,14 @@ def distri_async_groupnorm(g, groups, x_fresh, stale_moments, gamma=None, beta=N
         fresh_moments = torch.empty((g.batch, groups, 2), dtype=torch.float32, device=x_fresh.device)
     ws_bytes = distri_async_groupnorm_workspace_size(g, C, groups, code)
     ws, ws_len = _workspace(ws_bytes, x_fresh, workspace)
-    st = load().distri_async_groupnorm(
+    st = getattr(load(), func)(
         ctypes.byref(g), C, groups, float(eps), code, _ptr(x_fresh, "x_fresh", x_fresh.dtype),
         _ptr(stale_moments, "stale_moments", torch.float32, g.batch * g.n_patches * groups * 2),
         _ptr(gamma, "gamma", torch.float32, C), _ptr(beta, "beta", torch.float32, C),
         _ptr(y, "y", x_fresh.dtype, x_fresh.numel()),
         _ptr(fresh_moments, "fresh_moments", torch.float32, g.batch * groups * 2),
         _ptr(ws, "workspace"), ws_len, _stream(stream))
-    _check(st, "distri_async_groupnorm")
+    _check(st, func)
     return y, fresh_moments
 
 
@@ -276,4 +330,99 @@ def distri_patch_out_proj(g, o, w_o, bias=None, y=None, stream=None):
         ctypes.byref(g), C, code, _ptr(o, "o", o.dtype, n_tok), _ptr(w_o, "w_o", o.dtype, C * C),
         _ptr(bias, "bias", torch.float32, C), _ptr(y, "y", o.dtype, n_tok), _stream(stream))
     _check(st, "distri_patch_out_proj")
+    return y
+
+
+# ------------------------------------------------------------------ the block
+_WEIGHT_KEYS = ("gn1_gamma", "gn1_beta", "conv_w", "conv_b", "gn2_gamma", "gn2_beta", "w_qkv",
+                "b_qkv", "w_o", "b_o")
+_STATE_KEYS = ("gn1", "conv_in", "gn2", "k", "v")
+
+
+def _block_weights(weights, channels, groups, heads, eps, scale, dtype):
+    """BlockWeights from a dict of device tensors (fp32 vectors; conv_w
+    [C,3,3,C], w_qkv [3C,C], w_o [C,C] in the activation dtype)."""
+    C = channels
+    sizes = {"gn1_gamma": C, "gn1_beta": C, "conv_b": C, "gn2_gamma": C, "gn2_beta": C,
+             "b_qkv": 3 * C, "b_o": C, "conv_w": 9 * C * C, "w_qkv": 3 * C * C, "w_o": C * C}
+    bw = BlockWeights(int(channels), int(groups), int(heads), float(eps),
+                      float(scale if scale is not None else 64 ** -0.5))
+    for k in _WEIGHT_KEYS:
+        t = weights.get(k)
+        dt = dtype if k in ("conv_w", "w_qkv", "w_o") else torch.float32
+        setattr(bw, k, _ptr(t, k, dt, sizes[k]))
+    return bw
+
+
+def _block_state(state, g, channels, groups, dtype):
+    B, H, W, n = g.batch, g.height, g.width, g.n_patches
+    sizes = {"gn1": B * n * groups * 2, "gn2": B * n * groups * 2,
+             "conv_in": B * H * W * channels, "k": B * H * W * channels, "v": B * H * W * channels}
+    bs = BlockState()
+    for k in _STATE_KEYS:
+        dt = torch.float32 if k in ("gn1", "gn2") else dtype
+        setattr(bs, k, _ptr(state[k], "state " + k, dt, sizes[k]))
+    return bs
+
+
+def distri_patch_block_workspace_size(g, channels, groups, heads, dtype_code, sync=False) -> int:
+    bw = BlockWeights(int(channels), int(groups), int(heads), 1e-5, 0.125)
+    n = ctypes.c_size_t(0)
+    func = "distri_patch_block_sync_workspace_size" if sync else "distri_patch_block_workspace_size"
+    _check(getattr(load(), func)(ctypes.byref(_as_geom(g)), ctypes.byref(bw), dtype_code,
+                                 ctypes.byref(n)), func)
+    return int(n.value)
+
+
+def distri_patch_block_sync_workspace_size(g, channels, groups, heads, dtype_code) -> int:
+    return distri_patch_block_workspace_size(g, channels, groups, heads, dtype_code, sync=True)
+
+
+def distri_patch_block(g, weights, x, state_in, state_out=None, y=None, groups=32, heads=None,
+                       eps=1e-5, scale=None, workspace=None, stream=None):
+    """One asynchronous step of the block for patch i.  x [B,h,W,C] -> y
+    [B,Lq,C]; state_in / state_out: dicts with gn1, gn2 [B,n,G,2] fp32,
+    conv_in [B,H,W,C], k, v [B,H*W,C] (state_out defaults to state_in:
+    updated in place)."""
+    g = _as_geom(g)
+    code = _dtype_code(x)
+    C = x.shape[-1]
+    heads = C // 64 if heads is None else heads
+    if y is None:
+        y = torch.empty((g.batch, (g.height // max(g.n_patches, 1)) * g.width, C), dtype=x.dtype,
+                        device=x.device)
+    bw = _block_weights(weights, C, groups, heads, eps, scale, x.dtype)
+    sin = _block_state(state_in, g, C, groups, x.dtype)
+    sout = sin if state_out is None else _block_state(state_out, g, C, groups, x.dtype)
+    ws_bytes = distri_patch_block_workspace_size(g, C, groups, heads, code)
+    ws, ws_len = _workspace(ws_bytes, x, workspace)
+    st = load().distri_patch_block(
+        ctypes.byref(g), ctypes.byref(bw), code, _ptr(x, "x", x.dtype, y.numel()),
+        _ptr(y, "y", x.dtype, y.numel()), ctypes.byref(sin), ctypes.byref(sout),
+        _ptr(ws, "workspace"), ws_len, _stream(stream))
+    _check(st, "distri_patch_block")
+    return y
+
+
+def distri_patch_block_sync(g, weights, x, state, y=None, groups=32, heads=None, eps=1e-5,
+                            scale=None, workspace=None, stream=None):
+    """The synchronous (warm-up) step for all n patches on one device.
+    x [n, B, h, W, C] (patch-major) -> y [n, B, Lq, C]; fills ``state``."""
+    g = _as_geom(g)
+    code = _dtype_code(x)
+    C = x.shape[-1]
+    heads = C // 64 if heads is None else heads
+    n = g.n_patches
+    lq = (g.height // max(n, 1)) * g.width
+    if y is None:
+        y = torch.empty((n, g.batch, lq, C), dtype=x.dtype, device=x.device)
+    bw = _block_weights(weights, C, groups, heads, eps, scale, x.dtype)
+    bs = _block_state(state, g, C, groups, x.dtype)
+    ws_bytes = distri_patch_block_sync_workspace_size(g, C, groups, heads, code)
+    ws, ws_len = _workspace(ws_bytes, x, workspace)
+    st = load().distri_patch_block_sync(
+        ctypes.byref(g), ctypes.byref(bw), code, _ptr(x, "x", x.dtype, y.numel()),
+        _ptr(y, "y", x.dtype, y.numel()), ctypes.byref(bs), _ptr(ws, "workspace"), ws_len,
+        _stream(stream))
+    _check(st, "distri_patch_block_sync")
     return y

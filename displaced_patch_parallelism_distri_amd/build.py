@@ -2,7 +2,8 @@
 
 Usage: ``python -m displaced_patch_parallelism_distri_amd.build`` (or call
 ``build_library()``).  Compiles every ``csrc/*.hip`` file plus the C-ABI
-layer into one shared object next to this file.
+layer and the block runner (``csrc/*.cpp``, host code) into one shared
+object next to this file.
 """
 from __future__ import annotations
 
@@ -25,7 +26,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", 
 
 
 def sources():
-    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "abi.cpp")]
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + sorted(glob.glob(os.path.join(CSRC, "*.cpp")))
 
 
 def build_library(verbose: bool = False) -> str:

@@ -1,15 +1,7 @@
 // C ABI of the patch-layer library: host-side argument validation and
 // dispatch to the gfx950 kernels.  Every check runs before any HIP call, so a
 // rejected call enqueues nothing and touches no device state.
-#include "../../include/distri_patch.h"
-
-#include <hip/hip_runtime.h>
-
-#include <cmath>
-#include <cstdio>
-#include <cstring>
-
-#include "dp_common.h"
+#include "abi_check.h"
 
 namespace dp {
 
@@ -27,95 +19,50 @@ int device_cus() {
 
 }  // namespace dp
 
+namespace dp_abi {
+thread_local char g_last_error[256] = "";
+}  // namespace dp_abi
+
+using namespace dp_abi;
+
 namespace {
 
-thread_local char g_last_error[256] = "";
-
-int fail(int status, const char* fmt, const char* what) {
-    std::snprintf(g_last_error, sizeof(g_last_error), fmt, what);
-    return status;
-}
-
-#define DP_CHECK(cond, status, msg)                       \
-    do {                                                  \
-        if (!(cond)) return fail((status), "%s", (msg)); \
-    } while (0)
-
-int elem_bytes_of(int dtype) { return dtype == DISTRI_F32 ? 4 : 2; }
-
-// Geometry rules shared by every call.
-int check_geom(const distri_patch_geom* g) {
-    DP_CHECK(g != nullptr, DISTRI_ERR_NULL, "geometry pointer is NULL");
-    DP_CHECK(g->batch >= 0 && g->height >= 0 && g->width >= 0, DISTRI_ERR_SHAPE,
-             "batch, height and width must be >= 0");
-    DP_CHECK(g->n_patches >= 1, DISTRI_ERR_SHAPE, "n_patches must be >= 1");
-    DP_CHECK(g->patch >= 0 && g->patch < g->n_patches, DISTRI_ERR_SHAPE,
-             "patch must lie in [0, n_patches)");
-    DP_CHECK(g->height % g->n_patches == 0, DISTRI_ERR_SHAPE,
-             "height must be a multiple of n_patches");
-    DP_CHECK(g->batch <= 65535, DISTRI_ERR_UNSUPPORTED, "batch above 65535");
-    // keep every element offset far from int64 overflow
-    DP_CHECK(g->height <= (int64_t(1) << 24) && g->width <= (int64_t(1) << 24), DISTRI_ERR_UNSUPPORTED,
-             "height or width above 2^24");
-    return DISTRI_OK;
-}
-
-int check_dtype(int dtype) {
-    DP_CHECK(dtype == DISTRI_F32 || dtype == DISTRI_BF16, DISTRI_ERR_DTYPE,
-             "dtype must be DISTRI_F32 or DISTRI_BF16");
-    return DISTRI_OK;
-}
-
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
-
-struct Range {
-    const void* p;
-    size_t bytes;
-};
-bool overlaps(Range a, Range b) {
-    if (a.bytes == 0 || b.bytes == 0 || a.p == nullptr || b.p == nullptr) return false;
-    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
-    return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
-}
-
-dp::Geom to_geom(const distri_patch_geom* g) {
-    return dp::Geom{g->batch, g->height, g->width, g->n_patches, g->patch};
-}
-
-int hip_status(hipError_t e) {
-    if (e == hipSuccess) return DISTRI_OK;
-    std::snprintf(g_last_error, sizeof(g_last_error), "HIP error: %s", hipGetErrorString(e));
-    return DISTRI_ERR_HIP;
-}
-
-int check_attn_shape(const distri_patch_geom* g, int64_t heads, int64_t head_dim, int dtype) {
-    int st = check_geom(g);
+int groupnorm_entry(int mode, const distri_patch_geom* g, int64_t channels, int64_t groups,
+                    float eps, int dtype, const void* x_fresh, const float* stale_moments,
+                    const float* gamma, const float* beta, void* y, float* fresh_moments,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+    int st = check_gn_shape(g, channels, groups, dtype);
     if (st) return st;
-    st = check_dtype(dtype);
-    if (st) return st;
-    DP_CHECK(heads >= 1 && head_dim >= 1, DISTRI_ERR_SHAPE, "heads and head_dim must be >= 1");
-    DP_CHECK(heads <= 65535 / (g->batch > 0 ? g->batch : 1), DISTRI_ERR_UNSUPPORTED,
-             "batch * heads above 65535");
-    DP_CHECK(head_dim == 64, DISTRI_ERR_UNSUPPORTED, "head_dim must be 64");
-    // the kernels index one image's tokens with 32-bit offsets
-    DP_CHECK(g->height * g->width * heads * head_dim < (int64_t(1) << 31), DISTRI_ERR_UNSUPPORTED,
-             "height * width * heads * head_dim must stay below 2^31");
-    return DISTRI_OK;
-}
-
-int check_gn_shape(const distri_patch_geom* g, int64_t C, int64_t G, int dtype) {
-    int st = check_geom(g);
-    if (st) return st;
-    st = check_dtype(dtype);
-    if (st) return st;
-    DP_CHECK(C >= 1 && G >= 1 && C % G == 0, DISTRI_ERR_SHAPE,
-             "channels and groups must be >= 1 with channels % groups == 0");
-    const int vec = 16 / elem_bytes_of(dtype);
-    DP_CHECK(C % vec == 0, DISTRI_ERR_UNSUPPORTED,
-             "channels must be a multiple of 8 (bf16) or 4 (fp32)");
-    DP_CHECK(C / vec <= 512, DISTRI_ERR_UNSUPPORTED, "channels above 4096 (bf16) / 2048 (fp32)");
-    DP_CHECK(G <= 256, DISTRI_ERR_UNSUPPORTED, "more than 256 groups");
-    return DISTRI_OK;
+    DP_CHECK(std::isfinite(eps) && eps >= 0.f, DISTRI_ERR_SHAPE, "eps must be finite and >= 0");
+    const dp::Geom gg = to_geom(g);
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t xbytes = size_t(gg.B * gg.h() * gg.W * channels) * eb;
+    if (xbytes == 0) return DISTRI_OK;
+    DP_CHECK(x_fresh && stale_moments && y && fresh_moments, DISTRI_ERR_NULL,
+             "a tensor pointer is NULL");
+    DP_CHECK(aligned16(x_fresh) && aligned16(stale_moments) && aligned16(gamma) &&
+                 aligned16(beta) && aligned16(y) && aligned16(fresh_moments),
+             DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const size_t need = dp::groupnorm_workspace_bytes(gg, channels, groups, int(eb));
+    DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
+             "groupnorm workspace missing or too small");
+    DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
+    const size_t table = size_t(gg.B * gg.n * groups * 2) * 4;
+    const size_t fm = size_t(gg.B * groups * 2) * 4;
+    const size_t cb = size_t(channels) * 4;
+    const Range outs[3] = {{y, xbytes}, {fresh_moments, fm}, {workspace, need}};
+    const Range ins[4] = {{x_fresh, xbytes}, {stale_moments, table}, {gamma, gamma ? cb : 0},
+                          {beta, beta ? cb : 0}};
+    for (const Range& o : outs)
+        for (const Range& in : ins)
+            DP_CHECK(!overlaps(o, in), DISTRI_ERR_ALIAS, "an output overlaps an input");
+    DP_CHECK(!overlaps(outs[0], outs[1]) && !overlaps(outs[0], outs[2]) &&
+                 !overlaps(outs[1], outs[2]),
+             DISTRI_ERR_ALIAS, "outputs overlap each other");
+    return hip_status(dp::launch_groupnorm(gg, channels, groups, eps, dtype == DISTRI_BF16, mode,
+                                           x_fresh, stale_moments, gamma, beta, y, fresh_moments,
+                                           groups * 2, workspace,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -236,37 +183,48 @@ int distri_async_groupnorm(const distri_patch_geom* g, int64_t channels, int64_t
                            const float* stale_moments, const float* gamma, const float* beta,
                            void* y, float* fresh_moments, void* workspace,
                            size_t workspace_bytes, void* stream) {
+    return groupnorm_entry(dp::kGnNormalize, g, channels, groups, eps, dtype, x_fresh,
+                           stale_moments, gamma, beta, y, fresh_moments, workspace,
+                           workspace_bytes, stream);
+}
+
+int distri_async_groupnorm_silu(const distri_patch_geom* g, int64_t channels, int64_t groups,
+                                float eps, int dtype, const void* x_fresh,
+                                const float* stale_moments, const float* gamma,
+                                const float* beta, void* y, float* fresh_moments,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return groupnorm_entry(dp::kGnNormalizeSilu, g, channels, groups, eps, dtype, x_fresh,
+                           stale_moments, gamma, beta, y, fresh_moments, workspace,
+                           workspace_bytes, stream);
+}
+
+int distri_group_moments(const distri_patch_geom* g, int64_t channels, int64_t groups, int dtype,
+                         const void* x_fresh, float* table, void* workspace,
+                         size_t workspace_bytes, void* stream) {
     int st = check_gn_shape(g, channels, groups, dtype);
     if (st) return st;
-    DP_CHECK(std::isfinite(eps) && eps >= 0.f, DISTRI_ERR_SHAPE, "eps must be finite and >= 0");
     const dp::Geom gg = to_geom(g);
     const size_t eb = size_t(elem_bytes_of(dtype));
     const size_t xbytes = size_t(gg.B * gg.h() * gg.W * channels) * eb;
-    if (xbytes == 0) return DISTRI_OK;
-    DP_CHECK(x_fresh && stale_moments && y && fresh_moments, DISTRI_ERR_NULL,
-             "a tensor pointer is NULL");
-    DP_CHECK(aligned16(x_fresh) && aligned16(stale_moments) && aligned16(gamma) &&
-                 aligned16(beta) && aligned16(y) && aligned16(fresh_moments),
-             DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    if (gg.B == 0) return DISTRI_OK;
+    DP_CHECK(gg.h() * gg.W > 0, DISTRI_ERR_SHAPE, "the patch holds no pixels: moments undefined");
+    DP_CHECK(x_fresh && table, DISTRI_ERR_NULL, "a tensor pointer is NULL");
+    DP_CHECK(aligned16(x_fresh) && aligned16(table), DISTRI_ERR_ALIGN,
+             "tensor pointers must be 16-byte aligned");
     const size_t need = dp::groupnorm_workspace_bytes(gg, channels, groups, int(eb));
     DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
              "groupnorm workspace missing or too small");
     DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
-    const size_t table = size_t(gg.B * gg.n * groups * 2) * 4;
-    const size_t fm = size_t(gg.B * groups * 2) * 4;
-    const size_t cb = size_t(channels) * 4;
-    const Range outs[3] = {{y, xbytes}, {fresh_moments, fm}, {workspace, need}};
-    const Range ins[4] = {{x_fresh, xbytes}, {stale_moments, table}, {gamma, gamma ? cb : 0},
-                          {beta, beta ? cb : 0}};
-    for (const Range& o : outs)
-        for (const Range& in : ins)
-            DP_CHECK(!overlaps(o, in), DISTRI_ERR_ALIAS, "an output overlaps an input");
-    DP_CHECK(!overlaps(outs[0], outs[1]) && !overlaps(outs[0], outs[2]) &&
-                 !overlaps(outs[1], outs[2]),
-             DISTRI_ERR_ALIAS, "outputs overlap each other");
-    return hip_status(dp::launch_groupnorm(gg, channels, groups, eps, dtype == DISTRI_BF16,
-                                           x_fresh, stale_moments, gamma, beta, y, fresh_moments,
-                                           workspace, static_cast<hipStream_t>(stream)));
+    const size_t tbytes = size_t(gg.B * gg.n * groups * 2) * 4;
+    DP_CHECK(!overlaps({table, tbytes}, {x_fresh, xbytes}) &&
+                 !overlaps({workspace, need}, {x_fresh, xbytes}) &&
+                 !overlaps({workspace, need}, {table, tbytes}),
+             DISTRI_ERR_ALIAS, "table, workspace and x_fresh must not overlap");
+    return hip_status(dp::launch_groupnorm(gg, channels, groups, 0.f, dtype == DISTRI_BF16,
+                                           dp::kGnMomentsOnly, x_fresh, nullptr, nullptr, nullptr,
+                                           nullptr, table + gg.i * groups * 2,
+                                           gg.n * groups * 2, workspace,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int distri_refresh_stale(const distri_patch_geom* g, int64_t row_elems, int dtype,

@@ -88,10 +88,14 @@ hipError_t launch_refresh(const Geom& g, int64_t row_elems, int elem_bytes, cons
                           void* stale, hipStream_t s);
 
 size_t groupnorm_workspace_bytes(const Geom& g, int64_t C, int64_t G, int elem_bytes);
-hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool bf16,
+// mode: plain normalise, normalise then SiLU, or moments only (y, the
+// stale table and gamma / beta unused).  fresh_moments[b * fm_stride + 2g
+// + {0, 1}] receives (E[x], E[x^2]) of image b, group g over the slice.
+enum GnMode { kGnNormalize = 0, kGnNormalizeSilu = 1, kGnMomentsOnly = 2 };
+hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool bf16, int mode,
                             const void* x, const float* stale_moments, const float* gamma,
-                            const float* beta, void* y, float* fresh_moments, void* ws,
-                            hipStream_t s);
+                            const float* beta, void* y, float* fresh_moments, int64_t fm_stride,
+                            void* ws, hipStream_t s);
 
 size_t attention_workspace_bytes(const Geom& g, int64_t heads, bool bf16);
 hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16, const void* q,

@@ -22,7 +22,10 @@
 //                     per-channel affine a_c = rstd gamma_c,
 //                     b_c = beta_c - mu a_c (workspace [B][C][2]).  All of its
 //                     global loads are issued before any result is needed.
-//   3. gn_normalize - second coalesced pass: y = x a_c + b_c, rounded (RNE).
+//   3. gn_normalize - second coalesced pass: y = x a_c + b_c, optionally
+//                     followed by SiLU (y / (1 + e^-y), the activation that
+//                     follows GroupNorm in SDXL's ResNet blocks), rounded (RNE).
+// A moments-only form runs 1 and 2 and writes the patch's raw moments alone.
 // Deterministic: no atomics, every sum has a fixed order.  The second read of
 // x is normally served from L2 / the Infinity Cache: a chunk is read by the
 // same XCD in both passes and the slice is tens of MB.
@@ -115,6 +118,7 @@ struct GnArgs {
     const float* gamma;
     const float* beta;
     float* fresh_moments;
+    int64_t fm_stride;  // floats between images in fresh_moments
     GnWorkspace ws;
 };
 
@@ -124,6 +128,7 @@ struct GnArgs {
 constexpr int kFinThreads = 512;
 constexpr int kMaxChanPerThread = 8;  // C <= 4096
 
+template <bool MOMENTS_ONLY>
 __global__ __launch_bounds__(kFinThreads) void gn_finalize(GnArgs a) {
     extern __shared__ double red[];  // [slices][G][2], then (mu, rstd) [G][2]
     const int64_t b = blockIdx.x;
@@ -152,8 +157,10 @@ __global__ __launch_bounds__(kFinThreads) void gn_finalize(GnArgs a) {
     const uint64_t* tab = reinterpret_cast<const uint64_t*>(a.stale_moments) + b * a.n * G +
                           (tid < G ? tid : 0);
     uint64_t st[8];
+    if (!MOMENTS_ONLY) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) st[u] = tab[(u < a.n ? u : a.n - 1) * G];
+        for (int u = 0; u < 8; ++u) st[u] = tab[(u < a.n ? u : a.n - 1) * G];
+    }
     // thread (slice, g) adds chunks slice, slice + slices, ... in fp64 (16
     // loads in flight; the index is clamped and the extra terms dropped by a
     // select, so the loads need no branches); the slices are then added in
@@ -180,7 +187,7 @@ __global__ __launch_bounds__(kFinThreads) void gn_finalize(GnArgs a) {
         red[2 * (sl * G + g) + 1] = a2;
     }
     double st1 = 0.0, st2 = 0.0;
-    for (int64_t j0 = 0; j0 < a.n; j0 += 8) {
+    for (int64_t j0 = 0; j0 < (MOMENTS_ONLY ? 0 : a.n); j0 += 8) {
         if (j0 > 0) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) st[u] = tab[(j0 + u < a.n ? j0 + u : a.n - 1) * G];
@@ -201,8 +208,9 @@ __global__ __launch_bounds__(kFinThreads) void gn_finalize(GnArgs a) {
             s2 += red[2 * (sl * G + g) + 1];
         }
         const double m1 = s1 / a.count, m2 = s2 / a.count;
-        a.fresh_moments[(b * G + g) * 2 + 0] = float(m1);
-        a.fresh_moments[(b * G + g) * 2 + 1] = float(m2);
+        a.fresh_moments[b * a.fm_stride + g * 2 + 0] = float(m1);
+        a.fresh_moments[b * a.fm_stride + g * 2 + 1] = float(m2);
+        if (MOMENTS_ONLY) return;
         const double e1 = (m1 + st1) / double(a.n);
         const double e2 = (m2 + st2) / double(a.n);
         double var = e2 - e1 * e1;
@@ -210,6 +218,7 @@ __global__ __launch_bounds__(kFinThreads) void gn_finalize(GnArgs a) {
         stat[2 * g] = e1;
         stat[2 * g + 1] = 1.0 / sqrt(var + double(a.eps));
     }
+    if (MOMENTS_ONLY) return;
     __syncthreads();
     const int cg = a.C / G;
 #pragma unroll
@@ -276,7 +285,7 @@ __global__ __launch_bounds__(kMaxThreads) void gn_moments(GnArgs a) {
     }
 }
 
-template <class T, int KV>
+template <class T, int KV, bool SILU>
 __global__ __launch_bounds__(kMaxThreads) void gn_normalize(GnArgs a) {
     const int64_t b = blockIdx.y, chunk = blockIdx.x;
     const int tid = threadIdx.x;
@@ -297,15 +306,17 @@ __global__ __launch_bounds__(kMaxThreads) void gn_normalize(GnArgs a) {
             float f[T::VEC];
             T::unpack(v[k], f);
 #pragma unroll
-            for (int j = 0; j < T::VEC; ++j)
+            for (int j = 0; j < T::VEC; ++j) {
                 f[j] = fmaf(f[j], ab[j / 2][2 * (j % 2)], ab[j / 2][2 * (j % 2) + 1]);
+                if (SILU) f[j] = f[j] / (1.f + __expf(-f[j]));
+            }
             __builtin_nontemporal_store(T::pack(f), dst + (p0 + int64_t(k) * a.rows) * a.vpp);
         }
     }
 }
 
 template <class T, int KV>
-hipError_t run_kv(const GnPlan& p, const GnArgs& a, int64_t B, hipStream_t s) {
+hipError_t run_kv(const GnPlan& p, const GnArgs& a, int64_t B, int mode, hipStream_t s) {
     dim3 grid(unsigned(p.chunks), unsigned(B));
     const size_t lds = size_t(2) * p.rows * a.C * sizeof(float);
     hipLaunchKernelGGL((gn_moments<T, KV>), grid, dim3(p.threads), lds, s, a);
@@ -313,17 +324,24 @@ hipError_t run_kv(const GnPlan& p, const GnArgs& a, int64_t B, hipStream_t s) {
     if (e != hipSuccess) return e;
     const int slices = kFinThreads / a.G;
     const size_t lds_fin = (size_t(slices) * 2 * a.G + 2 * a.G) * sizeof(double);
-    hipLaunchKernelGGL(gn_finalize, dim3(unsigned(B)), dim3(kFinThreads), lds_fin, s, a);
+    if (mode == kGnMomentsOnly) {
+        hipLaunchKernelGGL(gn_finalize<true>, dim3(unsigned(B)), dim3(kFinThreads), lds_fin, s, a);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL(gn_finalize<false>, dim3(unsigned(B)), dim3(kFinThreads), lds_fin, s, a);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gn_normalize<T, KV>), grid, dim3(p.threads), 0, s, a);
+    if (mode == kGnNormalizeSilu)
+        hipLaunchKernelGGL((gn_normalize<T, KV, true>), grid, dim3(p.threads), 0, s, a);
+    else
+        hipLaunchKernelGGL((gn_normalize<T, KV, false>), grid, dim3(p.threads), 0, s, a);
     return hipGetLastError();
 }
 
 template <class T>
-hipError_t run(const Geom& g, int64_t C, int64_t G, float eps, const void* x,
+hipError_t run(const Geom& g, int64_t C, int64_t G, float eps, int mode, const void* x,
                const float* stale_moments, const float* gamma, const float* beta, void* y,
-               float* fresh_moments, void* ws, hipStream_t s) {
+               float* fresh_moments, int64_t fm_stride, void* ws, hipStream_t s) {
     const GnPlan p = plan_gn(g, C, int(sizeof(typename T::elem)));
     GnArgs a;
     a.x = x;
@@ -342,13 +360,14 @@ hipError_t run(const Geom& g, int64_t C, int64_t G, float eps, const void* x,
     a.gamma = gamma;
     a.beta = beta;
     a.fresh_moments = fresh_moments;
+    a.fm_stride = fm_stride;
     a.ws = carve(ws, g, p, C, G);
     switch (p.kv) {
-        case 1: return run_kv<T, 1>(p, a, g.B, s);
-        case 2: return run_kv<T, 2>(p, a, g.B, s);
-        case 4: return run_kv<T, 4>(p, a, g.B, s);
-        case 8: return run_kv<T, 8>(p, a, g.B, s);
-        default: return run_kv<T, kMaxKV>(p, a, g.B, s);
+        case 1: return run_kv<T, 1>(p, a, g.B, mode, s);
+        case 2: return run_kv<T, 2>(p, a, g.B, mode, s);
+        case 4: return run_kv<T, 4>(p, a, g.B, mode, s);
+        case 8: return run_kv<T, 8>(p, a, g.B, mode, s);
+        default: return run_kv<T, kMaxKV>(p, a, g.B, mode, s);
     }
 }
 
@@ -358,13 +377,15 @@ size_t groupnorm_workspace_bytes(const Geom& g, int64_t C, int64_t G, int elem_b
     return workspace_bytes(g, plan_gn(g, C, elem_bytes), C, G);
 }
 
-hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool bf16,
+hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool bf16, int mode,
                             const void* x, const float* stale_moments, const float* gamma,
-                            const float* beta, void* y, float* fresh_moments, void* ws,
-                            hipStream_t s) {
+                            const float* beta, void* y, float* fresh_moments, int64_t fm_stride,
+                            void* ws, hipStream_t s) {
     if (bf16)
-        return run<Bf16T>(g, C, G, eps, x, stale_moments, gamma, beta, y, fresh_moments, ws, s);
-    return run<F32T>(g, C, G, eps, x, stale_moments, gamma, beta, y, fresh_moments, ws, s);
+        return run<Bf16T>(g, C, G, eps, mode, x, stale_moments, gamma, beta, y, fresh_moments,
+                          fm_stride, ws, s);
+    return run<F32T>(g, C, G, eps, mode, x, stale_moments, gamma, beta, y, fresh_moments,
+                     fm_stride, ws, s);
 }
 
 }  // namespace dp

@@ -161,6 +161,39 @@ int distri_async_groupnorm(const distri_patch_geom *g, int64_t channels, int64_t
                            size_t workspace_bytes, void *stream);
 
 /*
+ * distri_async_groupnorm_silu - distri_async_groupnorm followed by SiLU,
+ * y = z / (1 + exp(-z)) with z the normalised, affine value (GroupNorm then
+ * SiLU opens each SDXL ResNet block, whose GroupNorm the wrapped module of the
+ * source walkthrough, item 3, replaces).  Same arguments, layouts, limits and
+ * workspace; y is rounded once from fp32.
+ */
+int distri_async_groupnorm_silu(const distri_patch_geom *g, int64_t channels, int64_t groups,
+                                float eps, int dtype, const void *x_fresh,
+                                const float *stale_moments, const float *gamma,
+                                const float *beta, void *y, float *fresh_moments,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * distri_group_moments - raw group moments of patch i written straight into
+ * its slot of a moment table:
+ *   table[b, i, g, :] = (E[x], E[x^2]) over the patch's h*W*(C/G) values
+ * Other slots are left unchanged.  This fills the table before the first
+ * asynchronous step and, in a synchronous step, shares every patch's current
+ * moments before any patch normalises (the first denoising steps run
+ * synchronously: README mirror, section 概述, figure (c), and the paper
+ * page's implementation details).  Same values as the fresh_moments of
+ * distri_async_groupnorm (same kernels, same summation order).
+ *
+ *   x_fresh  [B, h, W, C] dtype     table  [B, n, G, 2] fp32
+ *   workspace  >= distri_async_groupnorm_workspace_size() bytes
+ * Same channel and group limits as distri_async_groupnorm; a patch with no
+ * pixels (W == 0) is DISTRI_ERR_SHAPE.
+ */
+int distri_group_moments(const distri_patch_geom *g, int64_t channels, int64_t groups, int dtype,
+                         const void *x_fresh, float *table, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
+/*
  * distri_refresh_stale - make this step's fresh slice the next step's stale
  * context (the reuse of the previous step's activations, README mirror,
  * section 概述, figure (c)):
@@ -213,6 +246,81 @@ int distri_patch_qkv_proj(const distri_patch_geom *g, int64_t channels, int dtyp
 int distri_patch_out_proj(const distri_patch_geom *g, int64_t channels, int dtype,
                           const void *o, const void *w_o, const float *bias, void *y,
                           void *stream);
+
+/*
+ * Patch block: the wrapped layers chained at patch granularity for one
+ * denoising step (conv, self-attention and GroupNorm are the module types the
+ * source walkthrough wraps, section "Patch Parallelism的实现原理"):
+ *
+ *   g1 = SiLU(GN1(x))                  async GroupNorm, stale table gn1
+ *   h  = conv3x3(g1) + conv_b           halo rows from the stale map conv_in
+ *   n2 = GN2(h)                         async GroupNorm, stale table gn2
+ *   q, k, v = n2 w_qkv^T + b_qkv        K / V rows written into the k, v maps
+ *   o  = softmax(scale q K^T) V         K, V: this patch fresh, others stale
+ *   y  = o w_o^T + b_o
+ *
+ * Every stale read comes from state_in; this step's fresh values (g1 rows,
+ * GN moments, K and V rows) go to patch i's rows / slots of state_out, which
+ * become the next step's stale context.  state_out may be state_in itself
+ * (one device's buffers: a patch never reads its own stale rows), or a
+ * second set of buffers, so that all n patches of one step can run on one
+ * device against the same previous state.
+ */
+typedef struct {
+    int64_t channels; /* C = heads * 64 */
+    int64_t groups;   /* GroupNorm groups G (both norms) */
+    int64_t heads;
+    float eps;        /* GroupNorm eps */
+    float scale;      /* attention scale, > 0 (1/8 for head_dim 64) */
+    const float *gn1_gamma, *gn1_beta; /* [C] fp32 or NULL */
+    const void *conv_w;                /* [C, 3, 3, C] dtype */
+    const float *conv_b;               /* [C] fp32 or NULL */
+    const float *gn2_gamma, *gn2_beta; /* [C] fp32 or NULL */
+    const void *w_qkv;                 /* [3C, C] dtype: Q, K, V rows */
+    const float *b_qkv;                /* [3C] fp32 or NULL */
+    const void *w_o;                   /* [C, C] dtype */
+    const float *b_o;                  /* [C] fp32 or NULL */
+} distri_block_weights;
+
+typedef struct {
+    float *gn1;    /* [B, n, G, 2] fp32: per-patch raw moments of x */
+    void *conv_in; /* [B, H, W, C] dtype: g1 of every patch */
+    float *gn2;    /* [B, n, G, 2] fp32: per-patch raw moments of h */
+    void *k, *v;   /* [B, H*W, C] dtype */
+} distri_block_state;
+
+/*
+ * distri_patch_block - one asynchronous step of the block for patch i.
+ *   x [B, h, W, C] dtype -> y [B, Lq, C] dtype
+ * Limits: C = heads * 64, C % 64 == 0, the GroupNorm limits, and those of
+ * the ops above.  Every pointer 16-byte aligned.  The states' maps must not
+ * overlap x, y, the weights or the workspace, and state_out's maps must
+ * either be state_in's or not overlap them (DISTRI_ERR_ALIAS).
+ * workspace >= distri_patch_block_workspace_size() bytes.
+ */
+int distri_patch_block_workspace_size(const distri_patch_geom *g,
+                                      const distri_block_weights *w, int dtype, size_t *bytes);
+int distri_patch_block(const distri_patch_geom *g, const distri_block_weights *w, int dtype,
+                       const void *x, void *y, const distri_block_state *state_in,
+                       const distri_block_state *state_out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
+/*
+ * distri_patch_block_sync - the synchronous (warm-up) step of the block for
+ * all n patches on one device: before any patch reads another's activations
+ * of a stage, every patch has produced them, so the result is the block over
+ * the whole image, and afterwards `state` holds every patch's current values
+ * (the asynchronous steps' first stale context).  g->patch is ignored.
+ *   x  [n][B, h, W, C] dtype (patch-major)  ->  y  [n][B, Lq, C] dtype
+ *   state  as above; its previous contents are never read
+ * workspace >= distri_patch_block_sync_workspace_size() bytes.
+ */
+int distri_patch_block_sync_workspace_size(const distri_patch_geom *g,
+                                           const distri_block_weights *w, int dtype,
+                                           size_t *bytes);
+int distri_patch_block_sync(const distri_patch_geom *g, const distri_block_weights *w, int dtype,
+                            const void *x, void *y, const distri_block_state *state,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

@@ -200,3 +200,101 @@ def test_out_proj_rejects_bad_arguments(lib):
     assert call(bias=y + 256) == ALIAS
     assert call(geom=(2, 241, 240, 8, 4)) == SHAPE
     assert call(geom=(2, 240, 0, 8, 4), o=None, w=None, y=None) == OK
+
+
+def test_groupnorm_variants_reject_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    n = ctypes.c_size_t(0)
+    assert lib.distri_async_groupnorm_workspace_size(G(*g), 640, 32, BF16, ctypes.byref(n)) == OK
+    x, tab, y, fm, ws = (A + k * 64 * MB for k in range(5))
+    call = lambda **kw: lib.distri_async_groupnorm_silu(
+        G(*kw.get("geom", g)), kw.get("C", 640), kw.get("G", 32), kw.get("eps", 1e-5), BF16,
+        kw.get("x", x), kw.get("tab", tab), None, None, kw.get("y", y), kw.get("fm", fm),
+        kw.get("ws", ws), kw.get("wsb", n.value), None)
+    assert call(C=630) == SHAPE
+    assert call(G=512, C=1024) == UNSUP
+    assert call(tab=None) == NULL
+    assert call(wsb=n.value - 1) == WS
+    assert call(y=x + 64) == ALIAS
+    mom = lambda **kw: lib.distri_group_moments(
+        G(*kw.get("geom", g)), 640, 32, BF16, kw.get("x", x), kw.get("tab", tab), kw.get("ws", ws),
+        kw.get("wsb", n.value), None)
+    assert mom(tab=None) == NULL
+    assert mom(tab=tab + 4) == ALIGN
+    assert mom(wsb=0) == WS
+    assert mom(tab=x + 1024) == ALIAS
+    assert mom(ws=tab + 16) == ALIAS
+    assert mom(geom=(2, 240, 0, 8, 4)) == SHAPE
+    assert mom(geom=(0, 240, 240, 8, 4), x=None, tab=None, ws=None) == OK
+
+
+def _block_weights(C=640, G=32, heads=10, base=A):
+    w = dp.BlockWeights(C, G, heads, 1e-5, 0.125)
+    for k, name in enumerate(("gn1_gamma", "gn1_beta", "conv_w", "conv_b", "gn2_gamma", "gn2_beta",
+                              "w_qkv", "b_qkv", "w_o", "b_o")):
+        setattr(w, name, base + k * 64 * MB)
+    return w
+
+
+def _block_state(base):
+    s = dp.BlockState()
+    for k, name in enumerate(("gn1", "conv_in", "gn2", "k", "v")):
+        setattr(s, name, base + k * 1024 * MB)
+    return s
+
+
+def test_block_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    w = _block_weights()
+    sin, sout = _block_state(A + (1 << 40)), _block_state(A + (2 << 40))
+    x, y, ws = A + (3 << 40), A + (4 << 40), A + (5 << 40)
+    n = ctypes.c_size_t(0)
+    assert lib.distri_patch_block_workspace_size(G(*g), ctypes.byref(w), BF16, ctypes.byref(n)) == OK
+    ns = ctypes.c_size_t(0)
+    assert lib.distri_patch_block_sync_workspace_size(G(*g), ctypes.byref(w), BF16,
+                                                      ctypes.byref(ns)) == OK
+    assert ns.value > 4 * 2 * 240 * 240 * 640 * 2 > n.value > 5 * 2 * 30 * 240 * 640 * 2
+
+    def call(geom=g, w=w, dtype=BF16, x=x, y=y, sin=sin, sout=sout, ws=ws, wsb=None):
+        return lib.distri_patch_block(G(*geom), ctypes.byref(w) if w is not None else None, dtype, x,
+                                      y, ctypes.byref(sin) if sin is not None else None,
+                                      ctypes.byref(sout), ws, n.value if wsb is None else wsb, None)
+
+    assert call(w=None) == NULL
+    assert call(w=_block_weights(C=640, heads=8)) == SHAPE      # C != heads * 64
+    assert call(w=_block_weights(C=640, G=48)) == SHAPE         # C % G
+    assert call(dtype=4) == DTYPE
+    assert call(geom=(2, 240, 240, 7, 0)) == SHAPE
+    assert call(sin=None) == NULL
+    bad = _block_state(A + (1 << 40))
+    bad.k = None
+    assert call(sin=bad) == NULL
+    assert call(wsb=n.value - 1) == WS
+    assert call(x=x + 8) == ALIGN
+    w2 = _block_weights()
+    w2.eps = -1.0
+    assert call(w=w2) == SHAPE
+    w2 = _block_weights()
+    w2.scale = 0.0
+    assert call(w=w2) == SHAPE
+    w2 = _block_weights()
+    w2.w_o = None
+    assert call(w=w2) == NULL
+    assert call(y=x + 1024) == ALIAS                           # y inside x
+    assert call(ws=sin.k + 64) == ALIAS                         # workspace inside a stale map
+    part = _block_state(A + (2 << 40))
+    part.v = sin.v + 1024                                       # out map overlaps, not equal
+    assert call(sout=part) == ALIAS
+    part = _block_state(A + (2 << 40))
+    part.k = sin.v                                              # out k is in v: different field
+    assert call(sout=part) == ALIAS
+    assert call(geom=(0, 240, 240, 8, 4), x=None, y=None) == OK
+
+    def sync(wsb=ns.value, st=sout, x=x, y=y):
+        return lib.distri_patch_block_sync(G(*g), ctypes.byref(w), BF16, x, y, ctypes.byref(st),
+                                           ws, wsb, None)
+    assert sync(wsb=ns.value - 1) == WS
+    assert sync(y=x + 16) == ALIAS
+    same = _block_state(A + (2 << 40))
+    same.gn2 = same.gn1
+    assert sync(st=same) == ALIAS
