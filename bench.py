@@ -16,7 +16,11 @@ timed steps are graph replays (the eager step time is reported beside it).  Per-
 and refresh GB/s with buffers rotated through > 512 MB so the 256 MB
 Infinity Cache cannot serve them) ride along, plus the roofline of the
 dominant kernel (attention at level a) and the CPU oracle's rate on a bounded
-sample of the same workload.
+sample of the same workload.  Reported beside them, outside the step: the
+attention layer's Q/K/V (with the fused K/V refresh) and output projections
+in TFLOP/s, one asynchronous step of the chained patch block (GroupNorm+SiLU,
+halo conv, GroupNorm, projections, attention) and its synchronous warm-up
+step over all n patches.
 """
 from __future__ import annotations
 
@@ -195,6 +199,57 @@ def per_op(levels, iters):
             "conv_ms": cv_med, "conv_tflops": wl.conv_flops() / cv_med / 1e9,
             "attention_ms": at_med, "attention_tflops": wl.attn_flops() / at_med / 1e9,
         }
+        torch.cuda.empty_cache()
+    return res
+
+
+def block_bench(levels, iters):
+    """The attention layer's projections and the chained patch block at each
+    level (outside the step above): Q/K/V projection with its fused K/V
+    refresh and the output projection in TFLOP/s, one asynchronous block step
+    of this patch, and the synchronous warm-up step of all n patches."""
+    import torch
+
+    import displaced_patch_parallelism_distri_amd as dp
+    import synthetic_inputs as si
+
+    res = {}
+    for lv in levels:
+        wl = lv.wl
+        B, C, n, h, Lq = wl.batch, wl.channels, wl.n_patches, wl.h, wl.lq
+        M = B * Lq
+        d = si.make_block_inputs(wl, device="cuda")
+        w, st = d["weights"], d["state"]
+        x = d["x"][:, wl.patch * h:(wl.patch + 1) * h].contiguous()
+        xq = x.view(B, Lq, C)
+        q, k, v, o = (torch.empty(B, Lq, C, dtype=torch.bfloat16, device="cuda") for _ in range(4))
+        y = torch.empty_like(q)
+        qkv_ms, _ = time_op(lambda i: dp.distri_patch_qkv_proj(wl.geom, xq, w["w_qkv"], w["b_qkv"], q, k, v,
+                                                               st["k"], st["v"]), iters)
+        out_ms, _ = time_op(lambda i: dp.distri_patch_out_proj(wl.geom, xq, w["w_o"], w["b_o"], o), iters)
+        kw = dict(groups=wl.groups, heads=wl.heads, eps=wl.eps, scale=wl.head_dim ** -0.5)
+        ws = torch.empty(dp.distri_patch_block_workspace_size(wl.geom, C, wl.groups, wl.heads,
+                                                              dp.DISTRI_BF16), dtype=torch.uint8,
+                         device="cuda")
+        blk_ms, _ = time_op(lambda i: dp.distri_patch_block(wl.geom, w, x, st, y=y, workspace=ws, **kw),
+                            iters)
+        del ws
+        xp = d["x"].view(B, n, h, wl.width, C).transpose(0, 1).contiguous()
+        ys = torch.empty(n, B, Lq, C, dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(dp.distri_patch_block_sync_workspace_size(wl.geom, C, wl.groups, wl.heads,
+                                                                   dp.DISTRI_BF16), dtype=torch.uint8,
+                         device="cuda")
+        sync_ms, _ = time_op(lambda i: dp.distri_patch_block_sync(wl.geom, w, xp, st, y=ys, workspace=ws,
+                                                                  **kw), max(5, iters // 4))
+        qkv_fl, out_fl = 2.0 * M * 3 * C * C, 2.0 * M * C * C
+        blk_fl = wl.attn_flops() + wl.conv_flops() + qkv_fl + out_fl
+        res[wl.name] = {
+            "qkv_proj_ms": qkv_ms, "qkv_proj_tflops": qkv_fl / qkv_ms / 1e9,
+            "out_proj_ms": out_ms, "out_proj_tflops": out_fl / out_ms / 1e9,
+            "block_async_ms": blk_ms, "block_async_tflops": blk_fl / blk_ms / 1e9,
+            "block_sync_all_patches_ms": sync_ms,
+        }
+        del d, w, st, x, xp, ys, ws, q, k, v, o, y
         torch.cuda.empty_cache()
     return res
 
@@ -425,6 +480,7 @@ def main():
     value = flops / (step_ms * 1e-3) / 1e12
     ops = per_op(levels, args.op_iters)
     copy = copy_peak(args.op_iters)
+    blocks = block_bench(levels, args.op_iters)
 
     wa = levels[0].wl
     achieved = wa.attn_flops() / (attn_ms * 1e-3) / 1e12
@@ -450,6 +506,7 @@ def main():
         "per_op": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
         "groupnorm_gbps": {k: round(v["groupnorm_gbps"], 1) for k, v in ops.items()},
         "hbm_copy_peak": copy,
+        "projections_and_block": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in blocks.items()},
         "roofline": {"kernel": "attention at level a (attn_bf16_kernel + attn_combine_kernel)",
                      "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
