@@ -48,9 +48,10 @@ def _load():
         lib.oracle_linear.argtypes = [_I] * 3 + [_D] * 4
         lib.oracle_patch_qkv_proj.argtypes = [_I] * 6 + [_D] * 8
         lib.oracle_silu.argtypes = [_I, _D, _D]
+        lib.oracle_cross_attn.argtypes = [_I] * 5 + [ctypes.c_double] + [_D] * 4
         for f in ("oracle_patch_self_attn", "oracle_patch_conv3x3_halo", "oracle_group_moments",
                   "oracle_async_groupnorm", "oracle_refresh_stale", "oracle_linear",
-                  "oracle_patch_qkv_proj", "oracle_silu"):
+                  "oracle_patch_qkv_proj", "oracle_silu", "oracle_cross_attn"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -180,6 +181,18 @@ def patch_qkv_proj(geom, channels, x, w_qkv, bias=None, k_stale=None, v_stale=No
                                        _p(ks), _p(vs))
     _check(rc, "patch_qkv_proj")
     return q, k, v, ks, vs
+
+
+def cross_attn(scale, q, k_ctx, v_ctx):
+    """Patch queries q [B, Lq, heads, d] over a shared context k_ctx, v_ctx
+    [B, Lk, heads, d] -> [B, Lq, heads, d] float64."""
+    qf, kf, vf = _f64(q), _f64(k_ctx), _f64(v_ctx)
+    B, Lq, heads, d = qf.shape
+    Lk = kf.shape[1]
+    out = np.zeros((B, Lq, heads, d), dtype=np.float64)
+    _check(_load().oracle_cross_attn(B, Lq, Lk, heads, d, float(scale), _p(qf), _p(kf), _p(vf), _p(out)),
+           "cross_attn")
+    return out
 
 
 def silu(z):

@@ -353,3 +353,54 @@ int oracle_silu(int64_t n, const double *z, double *y)
     for (int64_t k = 0; k < n; ++k) y[k] = z[k] / (1.0 + exp(-z[k]));
     return 0;
 }
+
+/* Cross-attention of patch queries over a context that every patch shares
+ * (the text encoder's tokens; the wrapped cross-attention of the source
+ * walkthrough, section "Patch Parallelism的实现原理", item 2): for each image
+ * b, head and query row r,
+ *   out[b, r, head, :] = sum_t softmax_t(scale q[b, r, head, :] . k[b, t, head, :]) v[b, t, head, :]
+ * over the Lk context tokens.  Nothing is stale: the context is the same on
+ * every patch and every step.
+ *   q, out [B, Lq, heads, d]     k, v [B, Lk, heads, d] */
+int oracle_cross_attn(int64_t B, int64_t Lq, int64_t Lk, int64_t heads, int64_t d, double scale,
+                      const double *q, const double *k, const double *v, double *out)
+{
+    if (B < 0 || Lq < 0 || Lk <= 0 || heads <= 0 || d <= 0)
+        return -1;
+    int64_t task;
+#pragma omp parallel for schedule(dynamic, 16)
+    for (task = 0; task < B * heads * Lq; ++task) {
+        const int64_t b = task / (heads * Lq);
+        const int64_t hd = (task / Lq) % heads;
+        const int64_t r = task % Lq;
+        const double *qrow = q + ((b * Lq + r) * heads + hd) * d;
+        double *s = (double *)malloc(sizeof(double) * (size_t)Lk);
+        double m = -INFINITY;
+        for (int64_t t = 0; t < Lk; ++t) {
+            const double *krow = k + ((b * Lk + t) * heads + hd) * d;
+            double dot = 0.0;
+            for (int64_t e = 0; e < d; ++e)
+                dot += qrow[e] * krow[e];
+            s[t] = scale * dot;
+            if (s[t] > m)
+                m = s[t];
+        }
+        double denom = 0.0;
+        for (int64_t t = 0; t < Lk; ++t) {
+            s[t] = exp(s[t] - m);
+            denom += s[t];
+        }
+        double *orow = out + ((b * Lq + r) * heads + hd) * d;
+        for (int64_t e = 0; e < d; ++e)
+            orow[e] = 0.0;
+        for (int64_t t = 0; t < Lk; ++t) {
+            const double *vrow = v + ((b * Lk + t) * heads + hd) * d;
+            for (int64_t e = 0; e < d; ++e)
+                orow[e] += s[t] * vrow[e];
+        }
+        for (int64_t e = 0; e < d; ++e)
+            orow[e] /= denom;
+        free(s);
+    }
+    return 0;
+}
