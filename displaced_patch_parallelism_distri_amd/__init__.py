@@ -23,6 +23,7 @@ __all__ = [
     "distri_async_groupnorm_silu", "distri_group_moments", "distri_patch_block",
     "distri_patch_block_sync", "distri_patch_block_workspace_size",
     "distri_patch_block_sync_workspace_size", "BlockWeights", "BlockState",
+    "distri_patch_cross_attn", "distri_patch_cross_attn_workspace_size", "naive_geom",
     "DISTRI_F32", "DISTRI_BF16",
 ]
 
@@ -38,7 +39,8 @@ SYMBOLS = ("distri_abi_version", "distri_status_str", "distri_last_error",
            "distri_async_groupnorm", "distri_refresh_stale", "distri_patch_qkv_proj",
            "distri_patch_out_proj", "distri_async_groupnorm_silu", "distri_group_moments",
            "distri_patch_block_workspace_size", "distri_patch_block",
-           "distri_patch_block_sync_workspace_size", "distri_patch_block_sync")
+           "distri_patch_block_sync_workspace_size", "distri_patch_block_sync",
+           "distri_patch_cross_attn_workspace_size", "distri_patch_cross_attn")
 
 
 class DistriError(RuntimeError):
@@ -98,6 +100,8 @@ def load():
     lib.distri_patch_block_sync_workspace_size.argtypes = [G, BW, I, ctypes.POINTER(SZ)]
     lib.distri_patch_block.argtypes = [G, BW, I, P, P, BS, BS, P, SZ, P]
     lib.distri_patch_block_sync.argtypes = [G, BW, I, P, P, BS, P, SZ, P]
+    lib.distri_patch_cross_attn_workspace_size.argtypes = [G, I64, I64, I64, I, ctypes.POINTER(SZ)]
+    lib.distri_patch_cross_attn.argtypes = [G, I64, I64, I64, ctypes.c_float, I] + [P] * 5 + [SZ, P]
     for name in SYMBOLS[3:]:
         getattr(lib, name).restype = I
     _lib = lib
@@ -110,6 +114,15 @@ def abi_version() -> int:
 
 def geom(batch, height, width, n_patches, patch) -> Geom:
     return Geom(int(batch), int(height), int(width), int(n_patches), int(patch))
+
+
+def naive_geom(g) -> Geom:
+    """The naive-patch baseline's geometry for patch i of ``g``: the patch's
+    h rows taken as a whole image (n = 1), so every op sees this patch only:
+    attention over its own tokens, zero padding instead of a halo, GroupNorm
+    statistics of the patch alone (README mirror, section 概述, figure (b))."""
+    g = _as_geom(g)
+    return geom(g.batch, g.height // max(g.n_patches, 1), g.width, 1, 0)
 
 
 def _as_geom(g):
@@ -426,3 +439,35 @@ def distri_patch_block_sync(g, weights, x, state, y=None, groups=32, heads=None,
         _stream(stream))
     _check(st, "distri_patch_block_sync")
     return y
+
+
+def distri_patch_cross_attn_workspace_size(g, heads, ctx_len, dtype_code, head_dim=64) -> int:
+    n = ctypes.c_size_t(0)
+    _check(load().distri_patch_cross_attn_workspace_size(ctypes.byref(_as_geom(g)), heads, head_dim,
+                                                         ctx_len, dtype_code, ctypes.byref(n)),
+           "distri_patch_cross_attn_workspace_size")
+    return int(n.value)
+
+
+def distri_patch_cross_attn(g, heads, q, k_ctx, v_ctx, out=None, scale=None, head_dim=64,
+                            workspace=None, stream=None):
+    """Cross-attention of patch i: q [B, Lq, heads, d] over a shared context
+    k_ctx, v_ctx [B, ctx_len, heads, d] -> out [B, Lq, heads, d]."""
+    g = _as_geom(g)
+    code = _dtype_code(q)
+    ctx_len = k_ctx.shape[1]
+    if out is None:
+        out = torch.empty_like(q)
+    if scale is None:
+        scale = head_dim ** -0.5
+    lq = (g.height // max(g.n_patches, 1)) * g.width
+    nl = g.batch * lq * heads * head_dim
+    nc = g.batch * ctx_len * heads * head_dim
+    ws_bytes = distri_patch_cross_attn_workspace_size(g, heads, ctx_len, code, head_dim)
+    ws, ws_len = _workspace(ws_bytes, q, workspace)
+    st = load().distri_patch_cross_attn(
+        ctypes.byref(g), heads, head_dim, ctx_len, float(scale), code, _ptr(q, "q", q.dtype, nl),
+        _ptr(k_ctx, "k_ctx", q.dtype, nc), _ptr(v_ctx, "v_ctx", q.dtype, nc),
+        _ptr(out, "out", q.dtype, nl), _ptr(ws, "workspace"), ws_len, _stream(stream))
+    _check(st, "distri_patch_cross_attn")
+    return out

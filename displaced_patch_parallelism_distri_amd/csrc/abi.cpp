@@ -131,6 +131,50 @@ int distri_patch_self_attn(const distri_patch_geom* g, int64_t heads, int64_t he
                                            static_cast<hipStream_t>(stream)));
 }
 
+int distri_patch_cross_attn_workspace_size(const distri_patch_geom* g, int64_t heads,
+                                           int64_t head_dim, int64_t ctx_len, int dtype,
+                                           size_t* bytes) {
+    DP_CHECK(bytes != nullptr, DISTRI_ERR_NULL, "bytes pointer is NULL");
+    int st = check_cross_shape(g, heads, head_dim, ctx_len, dtype);
+    if (st) return st;
+    const dp::Geom gg = to_geom(g);
+    *bytes = dp::attention_workspace_bytes(gg.B, gg.lq(), ctx_len, heads, dtype == DISTRI_BF16);
+    return DISTRI_OK;
+}
+
+int distri_patch_cross_attn(const distri_patch_geom* g, int64_t heads, int64_t head_dim,
+                            int64_t ctx_len, float scale, int dtype, const void* q,
+                            const void* k_ctx, const void* v_ctx, void* out, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+    int st = check_cross_shape(g, heads, head_dim, ctx_len, dtype);
+    if (st) return st;
+    DP_CHECK(std::isfinite(scale) && scale > 0.f, DISTRI_ERR_SHAPE, "scale must be finite and > 0");
+    const dp::Geom gg = to_geom(g);
+    const size_t eb = size_t(elem_bytes_of(dtype));
+    const size_t local = size_t(gg.B * gg.lq() * heads * head_dim) * eb;
+    const size_t ctx = size_t(gg.B * ctx_len * heads * head_dim) * eb;
+    if (local == 0) return DISTRI_OK;
+    DP_CHECK(q && k_ctx && v_ctx && out, DISTRI_ERR_NULL, "a tensor pointer is NULL");
+    DP_CHECK(aligned16(q) && aligned16(k_ctx) && aligned16(v_ctx) && aligned16(out),
+             DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
+    const Range o{out, local};
+    DP_CHECK(!overlaps(o, {q, local}) && !overlaps(o, {k_ctx, ctx}) && !overlaps(o, {v_ctx, ctx}),
+             DISTRI_ERR_ALIAS, "out overlaps an input");
+    const size_t need = dp::attention_workspace_bytes(gg.B, gg.lq(), ctx_len, heads,
+                                                      dtype == DISTRI_BF16);
+    if (need > 0) {
+        DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
+                 "attention workspace missing or too small");
+        DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
+        DP_CHECK(!overlaps({workspace, need}, o), DISTRI_ERR_ALIAS, "workspace overlaps out");
+    }
+    // every key is a context token: the fresh range starts past the context
+    return hip_status(dp::launch_attention_rows(gg.B, gg.lq(), ctx_len, ctx_len, heads, scale,
+                                                dtype == DISTRI_BF16, q, k_ctx, v_ctx, k_ctx,
+                                                v_ctx, out, workspace,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int distri_patch_conv3x3_halo(const distri_patch_geom* g, int64_t c_in, int64_t c_out,
                               int dtype, const void* x_fresh, const void* x_stale,
                               const void* weight, const float* bias, void* y, void* stream) {

@@ -88,6 +88,24 @@ inline int check_attn_shape(const distri_patch_geom* g, int64_t heads, int64_t h
     return DISTRI_OK;
 }
 
+inline int check_cross_shape(const distri_patch_geom* g, int64_t heads, int64_t head_dim,
+                             int64_t ctx_len, int dtype) {
+    int st = check_geom(g);
+    if (st) return st;
+    st = check_dtype(dtype);
+    if (st) return st;
+    DP_CHECK(heads >= 1 && head_dim >= 1, DISTRI_ERR_SHAPE, "heads and head_dim must be >= 1");
+    DP_CHECK(ctx_len >= 1, DISTRI_ERR_SHAPE, "ctx_len must be >= 1");
+    DP_CHECK(heads <= 65535 / (g->batch > 0 ? g->batch : 1), DISTRI_ERR_UNSUPPORTED,
+             "batch * heads above 65535");
+    DP_CHECK(head_dim == 64, DISTRI_ERR_UNSUPPORTED, "head_dim must be 64");
+    const int64_t lq = (g->height / g->n_patches) * g->width;
+    DP_CHECK(lq * heads * head_dim < (int64_t(1) << 31) &&
+                 ctx_len * heads * head_dim < (int64_t(1) << 31),
+             DISTRI_ERR_UNSUPPORTED, "tokens * heads * head_dim must stay below 2^31");
+    return DISTRI_OK;
+}
+
 inline int check_gn_shape(const distri_patch_geom* g, int64_t C, int64_t G, int dtype) {
     int st = check_geom(g);
     if (st) return st;

@@ -525,18 +525,29 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgsF32 a) {
 
 }  // namespace
 
-size_t attention_workspace_bytes(const Geom& g, int64_t heads, bool bf16) {
+size_t attention_workspace_bytes(int64_t B, int64_t lq, int64_t L, int64_t heads, bool bf16) {
     if (!bf16) return 0;
     const int cus = device_cus();
     if (cus <= 0) return 0;
-    const Plan p = make_plan(g.B, heads, g.lq(), g.L(), cus);
+    const Plan p = make_plan(B, heads, lq, L, cus);
     return size_t(p.partials()) * QTILE * (D + 2) * sizeof(float);
+}
+
+size_t attention_workspace_bytes(const Geom& g, int64_t heads, bool bf16) {
+    return attention_workspace_bytes(g.B, g.lq(), g.L(), heads, bf16);
 }
 
 hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16, const void* q,
                             const void* kf, const void* vf, const void* ks, const void* vs,
                             void* out, void* ws, hipStream_t s) {
-    const int64_t lq = g.lq();
+    return launch_attention_rows(g.B, g.lq(), g.L(), g.i * g.lq(), heads, scale, bf16, q, kf, vf,
+                                 ks, vs, out, ws, s);
+}
+
+hipError_t launch_attention_rows(int64_t B, int64_t lq, int64_t L, int64_t own_lo, int64_t heads,
+                                 float scale, bool bf16, const void* q, const void* kf,
+                                 const void* vf, const void* ks, const void* vs, void* out,
+                                 void* ws, hipStream_t s) {
     if (bf16) {
         const int cus = device_cus();
         if (cus <= 0) return hipErrorNoDevice;
@@ -547,12 +558,12 @@ hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16
         a.ks = static_cast<const uint16_t*>(ks);
         a.vs = static_cast<const uint16_t*>(vs);
         a.out = static_cast<uint16_t*>(out);
-        a.plan = make_plan(g.B, heads, lq, g.L(), cus);
+        a.plan = make_plan(B, heads, lq, L, cus);
         a.part_o = static_cast<float*>(ws);
         a.part_ml = a.part_o + a.plan.partials() * D * QTILE;
         a.lq = int(lq);
-        a.L = int(g.L());
-        a.own_lo = int(g.i * lq);
+        a.L = int(L);
+        a.own_lo = int(own_lo);
         a.heads = int(heads);
         a.c = scale * 1.4426950408889634f;
         hipLaunchKernelGGL(attn_bf16_kernel, dim3(unsigned(a.plan.grid())), dim3(256), 0, s, a);
@@ -570,11 +581,11 @@ hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16
     a.vs = static_cast<const float*>(vs);
     a.out = static_cast<float*>(out);
     a.lq = lq;
-    a.L = g.L();
-    a.own_lo = g.i * lq;
+    a.L = L;
+    a.own_lo = own_lo;
     a.heads = int(heads);
     a.scale = scale;
-    dim3 grid(unsigned(ceil_div(lq, 64)), unsigned(g.B * heads));
+    dim3 grid(unsigned(ceil_div(lq, 64)), unsigned(B * heads));
     hipLaunchKernelGGL(attn_f32_kernel, grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }

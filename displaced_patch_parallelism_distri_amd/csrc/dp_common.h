@@ -98,9 +98,18 @@ hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool
                             void* ws, hipStream_t s);
 
 size_t attention_workspace_bytes(const Geom& g, int64_t heads, bool bf16);
+size_t attention_workspace_bytes(int64_t B, int64_t lq, int64_t L, int64_t heads, bool bf16);
 hipError_t launch_attention(const Geom& g, int64_t heads, float scale, bool bf16, const void* q,
                             const void* kf, const void* vf, const void* ks, const void* vs,
                             void* out, void* ws, hipStream_t s);
+// The same kernels with the token ranges given directly: lq queries per
+// image against L key/value tokens, of which [own_lo, own_lo + lq) come from
+// kf / vf ([B, lq, heads, 64]) and the rest from ks / vs ([B, L, heads, 64]).
+// own_lo >= L makes every key come from ks / vs (cross-attention).
+hipError_t launch_attention_rows(int64_t B, int64_t lq, int64_t L, int64_t own_lo, int64_t heads,
+                                 float scale, bool bf16, const void* q, const void* kf,
+                                 const void* vf, const void* ks, const void* vs, void* out,
+                                 void* ws, hipStream_t s);
 
 hipError_t launch_qkv_proj(const Geom& g, int64_t C, bool bf16, const void* x, const void* w_qkv,
                            const float* bias, void* q, void* k, void* v, void* k_stale,

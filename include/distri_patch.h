@@ -107,6 +107,30 @@ int distri_patch_self_attn(const distri_patch_geom *g, int64_t heads, int64_t he
                            void *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * distri_patch_cross_attn - cross-attention of patch i's queries over a
+ * context shared by every patch (the text encoder's tokens, already
+ * projected; the wrapped cross-attention of the source walkthrough, section
+ * "Patch Parallelism的实现原理", item 2).  Nothing in it is stale: the
+ * context is the same on every device and step, so a patch needs no other
+ * patch's data.  For every image b, head and local query r:
+ *   out[b, r, head, :] = softmax_t(scale * q[b, r, head, :] . k_ctx[b, t, head, :]) v_ctx
+ * over the ctx_len context tokens t.
+ *
+ *   q, out          [B, Lq, heads, head_dim]   dtype
+ *   k_ctx, v_ctx    [B, ctx_len, heads, head_dim] dtype
+ *   workspace       >= distri_patch_cross_attn_workspace_size() bytes
+ * head_dim must be 64 and ctx_len >= 1; same kernels and limits as
+ * distri_patch_self_attn, with L = ctx_len.
+ */
+int distri_patch_cross_attn_workspace_size(const distri_patch_geom *g, int64_t heads,
+                                           int64_t head_dim, int64_t ctx_len, int dtype,
+                                           size_t *bytes);
+int distri_patch_cross_attn(const distri_patch_geom *g, int64_t heads, int64_t head_dim,
+                            int64_t ctx_len, float scale, int dtype, const void *q,
+                            const void *k_ctx, const void *v_ctx, void *out, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/*
  * distri_patch_conv3x3_halo - 3x3 convolution (stride 1, zero padding 1) of
  * patch i (DistriConv2dPP, source walkthrough, item 1).  The input rows just
  * above and below the patch (the halo) come from the previous step's stale

@@ -244,3 +244,20 @@ def block_scalars(wl: Workload):
     """The block's non-tensor parameters at the shapes of ``wl``."""
     return {"channels": wl.channels, "groups": wl.groups, "heads": wl.heads, "eps": wl.eps,
             "scale": wl.head_dim ** -0.5}
+
+
+def make_cross_inputs(wl: Workload, ctx_len=77, device="cpu"):
+    """Seeded inputs of cross-attention with patch queries (own generator,
+    seeded with ``seed + 15485863``): q [B, Lq, heads, d] then k_ctx, v_ctx
+    [B, ctx_len, heads, d], all ~ N(0, 1), in the workload dtype.  77 is the
+    token count of SDXL's text encoders."""
+    g = torch.Generator(device=device)
+    g.manual_seed(wl.seed + 15485863)
+    B, nh, d = wl.batch, wl.heads, wl.head_dim
+    dt = wl.torch_dtype
+
+    def randn(*shape):
+        return torch.randn(*shape, generator=g, device=device, dtype=torch.float32).to(dt).contiguous()
+
+    return {"q": randn(B, wl.lq, nh, d), "k_ctx": randn(B, ctx_len, nh, d),
+            "v_ctx": randn(B, ctx_len, nh, d)}

@@ -298,3 +298,26 @@ def test_block_rejects_bad_arguments(lib):
     same = _block_state(A + (2 << 40))
     same.gn2 = same.gn1
     assert sync(st=same) == ALIAS
+
+
+def test_cross_attention_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    q, k, v, o = (A + j * 64 * MB for j in range(4))
+
+    def call(geom=g, heads=10, hd=64, ctx=77, scale=0.125, dtype=BF16, q=q, k=k, v=v, o=o, ws=None,
+             wsb=0):
+        return lib.distri_patch_cross_attn(G(*geom), heads, hd, ctx, scale, dtype, q, k, v, o, ws, wsb,
+                                           None)
+
+    assert call(ctx=0) == SHAPE
+    assert call(hd=32) == UNSUP
+    assert call(heads=0) == SHAPE
+    assert call(scale=-1.0) == SHAPE
+    assert call(dtype=2) == DTYPE
+    assert call(k=None) == NULL
+    assert call(v=v + 4) == ALIGN
+    assert call(o=k + 64) == ALIAS
+    assert call(geom=(0, 240, 240, 8, 4), q=None, k=None, v=None, o=None) == OK
+    n = ctypes.c_size_t(0)
+    assert lib.distri_patch_cross_attn_workspace_size(G(*g), 10, 64, 77, BF16, ctypes.byref(n)) == OK
+    assert lib.distri_patch_cross_attn_workspace_size(G(*g), 10, 64, 0, BF16, ctypes.byref(n)) == SHAPE
