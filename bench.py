@@ -20,7 +20,9 @@ sample of the same workload.  Reported beside them, outside the step: the
 attention layer's Q/K/V (with the fused K/V refresh) and output projections
 in TFLOP/s, one asynchronous step of the chained patch block (GroupNorm+SiLU,
 halo conv, GroupNorm, projections, attention) and its synchronous warm-up
-step over all n patches.
+step over all n patches; cross-attention of the patch queries over a 77-token
+context; and the naive-patch layer (each op on this patch alone) for
+comparison.
 """
 from __future__ import annotations
 
@@ -241,6 +243,28 @@ def block_bench(levels, iters):
                          device="cuda")
         sync_ms, _ = time_op(lambda i: dp.distri_patch_block_sync(wl.geom, w, xp, st, y=ys, workspace=ws,
                                                                   **kw), max(5, iters // 4))
+        # cross-attention of the patch queries over a 77-token context, and
+        # the naive-patch layer (each op on this patch alone)
+        cx = si.make_cross_inputs(wl, 77, device="cuda")
+        co = torch.empty_like(cx["q"])
+        cws = torch.empty(max(1, dp.distri_patch_cross_attn_workspace_size(wl.geom, wl.heads, 77,
+                                                                           dp.DISTRI_BF16)),
+                          dtype=torch.uint8, device="cuda")
+        cx_ms, _ = time_op(lambda i: dp.distri_patch_cross_attn(wl.geom, wl.heads, cx["q"], cx["k_ctx"],
+                                                                cx["v_ctx"], out=co, workspace=cws), iters)
+        cx_bytes = 2 * (cx["q"].numel() + 2 * cx["k_ctx"].numel())
+        cx_fl = 4.0 * B * wl.heads * Lq * 77 * wl.head_dim
+        del cx, co, cws
+        ng = dp.naive_geom(wl.geom)
+        t = lv.t
+        zt = torch.zeros(B, 1, wl.groups, 2, device="cuda")
+
+        def naive_layer(i):
+            yg, _ = dp.distri_async_groupnorm(ng, wl.groups, t["x_fresh"], zt, t["gamma"], t["beta"])
+            dp.distri_patch_conv3x3_halo(ng, yg, None, t["weight"], t["bias"])
+            dp.distri_patch_self_attn(ng, wl.heads, t["q"], t["k_fresh"], t["v_fresh"], t["k_fresh"],
+                                      t["v_fresh"])
+        naive_ms, _ = time_op(naive_layer, iters)
         qkv_fl, out_fl = 2.0 * M * 3 * C * C, 2.0 * M * C * C
         blk_fl = wl.attn_flops() + wl.conv_flops() + qkv_fl + out_fl
         res[wl.name] = {
@@ -248,6 +272,9 @@ def block_bench(levels, iters):
             "out_proj_ms": out_ms, "out_proj_tflops": out_fl / out_ms / 1e9,
             "block_async_ms": blk_ms, "block_async_tflops": blk_fl / blk_ms / 1e9,
             "block_sync_all_patches_ms": sync_ms,
+            "cross_attn_ctx77_ms": cx_ms, "cross_attn_ctx77_tflops": cx_fl / cx_ms / 1e9,
+            "cross_attn_ctx77_gbps": cx_bytes / cx_ms / 1e6,
+            "naive_patch_layer_ms": naive_ms,
         }
         del d, w, st, x, xp, ys, ws, q, k, v, o, y
         torch.cuda.empty_cache()
