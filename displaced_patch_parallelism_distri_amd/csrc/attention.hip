@@ -29,11 +29,13 @@
 //    a lane then holds 16 keys of ONE query per 32x32 block, so the row max and
 //    row sum are in-lane reductions plus one exchange between the two
 //    half-waves;
-//  * online softmax in the log2 domain (exp2(s*scale*log2e - m)) with a lazy
-//    running max: the reference m moves (and O and l are rescaled, a
-//    wave-uniform branch) only when some row of the wave exceeds it by more
-//    than kLazy, so after the first tile long key loops almost never
-//    rescale.  P is then at most 2^kLazy, which bf16 and the fp32
+//  * online softmax in the log2 domain (exp2(s*scale*log2e - m)) against a
+//    reference max m that moves only when needed: each tile first forms P
+//    with the current m and no row max at all; only if some lane's sum of P
+//    leaves [0, kSumLimit] (the first tile, where m = -inf, or a score above
+//    m by about log2(kSumLimit)) does the wave take a rare, wave-uniform
+//    branch that forms S again, takes the row max, rescales O and l and
+//    recomputes P.  P then stays at most kSumLimit, which bf16 and the fp32
 //    accumulators carry with the same relative precision.  The row sum l
 //    adds the bf16-rounded P (v_dot2_f32_bf16) so numerator and denominator
 //    carry the same rounding - a row dominated by one key then returns that
@@ -60,7 +62,7 @@ constexpr int QTILE = NWAVES * QB * 32;
 constexpr int KPITCH = D + 8;   // LDS row pitch of K (bf16 elements)
 constexpr int VPITCH = KT + 4;  // LDS row pitch of V^T (bf16 elements)
 constexpr int kPartialCost = 3; // cost of one partial write + merge, in key tiles
-constexpr float kLazy = 8.0f;   // log2-domain slack of the running max
+constexpr float kSumLimit = 4096.0f;  // largest lane sum of P kept without moving the max
 
 // Work plan shared by the host launcher and both kernels.
 struct Plan {
@@ -250,113 +252,134 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // a map whose Lq is not a multiple of 256) only loads and syncs, which
     // leaves its SIMD to the other block on the CU.
     const bool wave_active = q0 < a.lq;
+    // S^T = K Q^T of LDS stage `cur` for query blocks qb in [q_lo, q_hi):
+    // s[kb][qb] covers keys kb*32.. and queries qb*32..; keys past the map
+    // (kMask) get -inf
+    auto qk = [&](int cur, int kt, f32x16 (&s)[2][QB], int q_lo, int q_hi, auto kMask) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
+                    &k_lds[cur][(kb * 32 + lr) * KPITCH + ks * 16 + g * 8]);
+#pragma unroll
+                for (int qb = q_lo; qb < q_hi; ++qb)
+                    s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        ka, qf[qb][ks], ks == 0 ? f32x16{} : s[kb][qb], 0, 0, 0);
+            }
+        }
+        if (decltype(kMask)::value) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int key = kt * KT + kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
+                    if (key >= a.L)
+#pragma unroll
+                        for (int qb = q_lo; qb < q_hi; ++qb) s[kb][qb][j] = -INFINITY;
+                }
+        }
+    };
+    // P = exp2(s * c - m[qb]) rounded to bf16, and the lane's sum of those
+    // rounded values (the row sum adds the bf16-rounded p that the PV MFMA
+    // multiplies, so the normalisation matches the numerator)
+    auto softmax = [&](const f32x16 (&s)[2][QB], int qb, bf16x8 (&p)[2][2]) {
+        const float mneg = -m[qb];
+        float rsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[e] = pack_bf16x2(
+                        __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.c, mneg)),
+                        __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.c, mneg)));
+                // (scalar words on purpose: passing vector elements w[e]
+                // straight to the builtin made hipcc read w[0] four times)
+                const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
+                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rsum, false);
+                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rsum, false);
+                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rsum, false);
+                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rsum, false);
+                p[kb][h2] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+            }
+        }
+        return rsum;
+    };
+
+    // one key tile: prefetch the next tile into registers, S^T on MFMA, then
+    // per 32-query block the online softmax and PV on MFMA (the PV of one
+    // block overlaps the softmax of the next), then stage the prefetched tile
+    // in LDS.  kMask (a std::integral_constant) masks keys past the end of
+    // the map; only the map's last, partial tile needs it.
+    // A wave whose 64 queries all lie past the patch (the last query tile of
+    // a map whose Lq is not a multiple of 256) only loads and syncs, which
+    // leaves its SIMD to the other block on the CU.
     auto tile = [&](int kt, auto kMask) {
         const int cur = (kt - kt0) & 1;
         if (kt + 1 < kt1) gload(kt + 1);
         if (wave_active) {
-            // S^T = K Q^T : s[kb][qb] covers keys kb*32.. and queries qb*32..
             f32x16 s[2][QB];
+            // one query block after the other, so that the second block's
+            // MFMAs can overlap the first block's softmax
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-                        &k_lds[cur][(kb * 32 + lr) * KPITCH + ks * 16 + g * 8]);
-#pragma unroll
-                    for (int qb = 0; qb < QB; ++qb)
-                        s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            ka, qf[qb][ks], ks == 0 ? f32x16{} : s[kb][qb], 0, 0, 0);
-                }
-            }
-            if (decltype(kMask)::value) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) {
-                        const int key = kt * KT + kb * 32 + 8 * (j >> 2) + 4 * g + (j & 3);
-                        if (key >= a.L)
-#pragma unroll
-                            for (int qb = 0; qb < QB; ++qb) s[kb][qb][j] = -INFINITY;
-                    }
-            }
-
-            bf16x8 p[2][QB][2];
+            for (int qb = 0; qb < QB; ++qb) qk(cur, kt, s, qb, qb + 1, kMask);
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
-                float mx = s[0][qb][0];
+                // fast path: P against the current reference max, no row max
+                bf16x8 p[2][2];
+                float rsum = softmax(s, qb, p);
+                // the reference max moves only when some lane's sum of P
+                // leaves [0, kSumLimit] (always on the first tile, where m =
+                // -inf, and whenever a score exceeds m by about
+                // log2(kSumLimit)): then this block's S is formed again, the
+                // row max taken, O and l rescaled and P recomputed.  A
+                // wave-uniform, rare branch; S is recomputed rather than kept
+                // so that it holds no registers across the fast path.
+                if (__any(!(rsum <= kSumLimit))) {
+                    qk(cur, kt, s, qb, qb + 1, kMask);
+                    float mx = s[0][qb][0];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, s[kb][qb][j]);
-                // the other half-wave holds the other 16 keys of each 32-key block
-                // the other half-wave holds the other 16 keys of each 32-key block
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                                 false, false);
-                mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.c;
-                // lazy running max: keep the reference m until some row of the
-                // wave exceeds it by more than kLazy (always on the first tile,
-                // where m = -inf); then rescale O and l (wave-uniform branch)
-                if (__any(mx > m[qb] + kLazy)) {
+                        for (int j = 0; j < 16; ++j) mx = __builtin_fmaxf(mx, s[kb][qb][j]);
+                    // the other half-wave holds the other 16 keys of each 32-key block
+                    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                                     __float_as_uint(mx), false, false);
+                    mx = __builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.c;
                     const float mnew = __builtin_fmaxf(m[qb], mx);
                     const float alpha = __builtin_amdgcn_exp2f(m[qb] - mnew);
                     l[qb] *= alpha;
 #pragma unroll
                     for (int db = 0; db < 2; ++db) o[db][qb] *= alpha;
                     m[qb] = mnew;
+                    rsum = softmax(s, qb, p);
                 }
-                const float mneg = -m[qb];
-                float rsum = 0.f;
+                l[qb] += rsum;
+
+                // O^T += V^T P^T.  B operand slot e of k-step (kb, h2) holds
+                // key kb*32 + h2*16 + (e/4)*8 + 4g + e%4 (the S^T accumulator
+                // layout), so the V^T operand reads those same keys: two
+                // 4-key runs.
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                     for (int h2 = 0; h2 < 2; ++h2) {
-                        uint32_t w[4];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            w[e] = pack_bf16x2(
-                                __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.c, mneg)),
-                                __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.c, mneg)));
-                        // the row sum adds the bf16-rounded p that the PV MFMA
-                        // multiplies, so the normalisation matches the numerator.
-                        // (Scalar words on purpose: passing vector elements w[e]
-                        // straight to the builtin made hipcc read w[0] four times.)
-                        const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-                        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes,
-                                                               rsum, false);
-                        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes,
-                                                               rsum, false);
-                        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes,
-                                                               rsum, false);
-                        rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes,
-                                                               rsum, false);
-                        p[kb][qb][h2] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
-                    }
-                }
-                l[qb] += rsum;
-            }
-
-            // O^T += V^T P^T.  B operand slot e of k-step (kb, h2) holds key
-            // kb*32 + h2*16 + (e/4)*8 + 4g + e%4 (the S^T accumulator layout), so
-            // the V^T operand reads those same keys: two 4-key runs.
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-#pragma unroll
-                    for (int db = 0; db < 2; ++db) {
-                        const uint16_t* vp =
-                            &v_lds[cur][(db * 32 + lr) * VPITCH + kb * 32 + h2 * 16 + 4 * g];
-                        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vp);
-                        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vp + 8);
-                        const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-                        for (int qb = 0; qb < QB; ++qb)
-                            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kb][qb][h2],
-                                                                                o[db][qb], 0, 0, 0);
+                        for (int db = 0; db < 2; ++db) {
+                            const uint16_t* vp =
+                                &v_lds[cur][(db * 32 + lr) * VPITCH + kb * 32 + h2 * 16 + 4 * g];
+                            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vp);
+                            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vp + 8);
+                            const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kb][h2], o[db][qb],
+                                                                                0, 0, 0);
+                        }
                     }
                 }
             }
-
         }
         if (kt + 1 < kt1) lstore(cur ^ 1);
         __syncthreads();
