@@ -86,3 +86,66 @@ def test_layer_graph_replays_match_eager():
         junk = torch.randn(1 << 20, device=dev).sum()
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
+
+
+def test_block_and_cross_attention_graph_replays_match_eager():
+    """The chained block (in-place state) and a cross-attention call captured
+    once: every replay equals the eager calls.  (A patch never reads its own
+    stale rows or slots, so a second step on the same input writes the same
+    state and returns the same output.)"""
+    wl = si.WORKLOADS["sdxl1024_l2"].with_patch(5)
+    dev = torch.device("cuda:0")
+    d = si.make_block_inputs(wl, device=dev)
+    cx = si.make_cross_inputs(wl, 77, device=dev)
+    h, i = wl.h, wl.patch
+    x = d["x"][:, i * h:(i + 1) * h].contiguous()
+    kw = dict(groups=wl.groups, heads=wl.heads, eps=wl.eps, scale=0.125)
+    ws = torch.empty(dp.distri_patch_block_workspace_size(wl.geom, wl.channels, wl.groups, wl.heads,
+                                                          dp.DISTRI_BF16), dtype=torch.uint8, device=dev)
+    cws = torch.empty(max(1, dp.distri_patch_cross_attn_workspace_size(wl.geom, wl.heads, 77, dp.DISTRI_BF16)),
+                      dtype=torch.uint8, device=dev)
+
+    def make_state():
+        st = {k: v.clone() for k, v in d["state"].items()}
+        st["y"] = torch.empty(wl.batch, wl.lq, wl.channels, dtype=torch.bfloat16, device=dev)
+        st["c"] = torch.empty_like(cx["q"])
+        return st
+
+    def step(st):
+        dp.distri_patch_block(wl.geom, d["weights"], x, st, y=st["y"], workspace=ws, **kw)
+        dp.distri_patch_cross_attn(wl.geom, wl.heads, cx["q"], cx["k_ctx"], cx["v_ctx"], out=st["c"],
+                                   workspace=cws)
+
+    ref = make_state()
+    step(ref)
+    torch.cuda.synchronize()
+    first = {k: v.clone() for k, v in ref.items()}
+    step(ref)
+    torch.cuda.synchronize()
+    second = {k: v.clone() for k, v in ref.items()}
+    for k in first:
+        assert torch.equal(_bits(first[k]), _bits(second[k])), k
+
+    st = make_state()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    warm = make_state()
+    with torch.cuda.stream(side):
+        step(warm)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(st)
+    for k, v in make_state().items():
+        st[k].copy_(v)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        g.replay()
+        torch.cuda.synchronize()
+        want = first if rep == 0 else second
+        for k in st:
+            assert torch.equal(_bits(st[k]), _bits(want[k])), f"replay {rep}: {k} differs from eager"
+        junk = torch.randn(1 << 20, device=dev).sum()
+        torch.cuda.synchronize()
+        assert torch.isfinite(junk)
