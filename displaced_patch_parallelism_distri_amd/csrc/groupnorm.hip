@@ -35,7 +35,7 @@
 namespace dp {
 namespace {
 
-constexpr int kTargetBlocks = 512;
+constexpr int kTargetBlocks = 256;
 constexpr int kMaxThreads = 512;
 constexpr int kMaxKV = 16;
 
