@@ -42,6 +42,11 @@ constexpr int BN = 160, BK = 64;
 constexpr int WN = 80, NT = WN / 16;  // wave tile columns, 16-wide MFMA tiles
 constexpr int B_CHUNKS = BN * 8 / 256;  // 16-byte chunks per thread per step
 
+// The zero padding's source: an A row of a padded tap (outside the image, or
+// a halo row at the image edge) reads its channels [0, Cin) from here, so the
+// loaded values go to LDS without a select.  Never written; Cin <= 65536.
+__device__ __attribute__((aligned(16))) uint16_t conv_zeros[65536];
+
 struct ConvArgs {
     const uint16_t* xf;
     const uint16_t* xs;
@@ -95,8 +100,7 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
         ar[j] = rem / a.W;
         acol[j] = rem - ar[j] * a.W;
     }
-    const uint16_t* aptr[A_CHUNKS];  // pixel base of the current tap (or x_fresh)
-    bool aok[A_CHUNKS];
+    const uint16_t* aptr[A_CHUNKS];  // pixel base of the current tap (or the zeros)
     auto set_tap = [&](int tap) {
         const int kh = tap / 3, kw = tap - kh * 3;
 #pragma unroll
@@ -113,8 +117,7 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
                 ok = ok && a.i < a.n - 1;
                 p = a.xs + ((size_t(ab[j]) * a.H + size_t(a.i + 1) * a.h) * a.W + cc) * a.cin;
             }
-            aok[j] = ok;
-            aptr[j] = ok ? p : a.xf;
+            aptr[j] = ok ? p : conv_zeros;
         }
     };
 
@@ -132,21 +135,18 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
     const int nsteps = 9 * kchunks;
     // Two register sets: the loads of step s + 2 are issued while step s
     // computes, and step s + 1's values (loaded a step earlier) are stored to
-    // LDS at the end of step s.  Loaded values stay raw until they are
-    // stored: the zero select for padding / out-of-range rows is applied
-    // there, so nothing waits on the loads while the MFMAs run.
+    // LDS at the end of step s.  Padding rows already read zeros and weight
+    // rows past Cout read row 0's weights (they feed only output columns that
+    // are never stored), so the values go to LDS as loaded.
     u32x4 areg[2][A_CHUNKS], breg[2][B_CHUNKS];
-    bool amask[2][A_CHUNKS];
     auto gload = [&](int s, auto set) {
         constexpr int R = decltype(set)::value;
         const int tap = s / kchunks;
         const int ci0 = (s - tap * kchunks) * BK;
         if (ci0 == 0) set_tap(tap);
 #pragma unroll
-        for (int j = 0; j < A_CHUNKS; ++j) {
+        for (int j = 0; j < A_CHUNKS; ++j)
             areg[R][j] = *reinterpret_cast<const u32x4*>(aptr[j] + ci0 + akc * 8);
-            amask[R][j] = aok[j];
-        }
 #pragma unroll
         for (int j = 0; j < B_CHUNKS; ++j)
             breg[R][j] = *reinterpret_cast<const u32x4*>(bptr[j] + tap * a.cin + ci0);
@@ -156,14 +156,12 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
 #pragma unroll
         for (int j = 0; j < A_CHUNKS; ++j) {
             const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&a_lds[buf][row * BK + swz(row, akc) * 8]) =
-                amask[R][j] ? areg[R][j] : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(&a_lds[buf][row * BK + swz(row, akc) * 8]) = areg[R][j];
         }
 #pragma unroll
         for (int j = 0; j < B_CHUNKS; ++j) {
             const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&b_lds[buf][row * BK + swz(row, akc) * 8]) =
-                bok[j] ? breg[R][j] : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(&b_lds[buf][row * BK + swz(row, akc) * 8]) = breg[R][j];
         }
     };
 

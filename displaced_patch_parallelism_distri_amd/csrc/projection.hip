@@ -80,7 +80,7 @@ __global__ __launch_bounds__(256, 2) void proj_bf16_kernel(ProjArgs a) {
     const int m0 = mt * BM, n0 = nt * BN;
 
     // loaders: chunk c = tid + 256 j -> row c / 8, 16-byte chunk c % 8; rows
-    // past M / N re-read row 0 and are zeroed at the LDS store
+    // past M / N re-read row 0: they feed only outputs that are never stored
     const int akc = tid & 7;
     const uint16_t* aptr[A_CHUNKS];
     bool aok[A_CHUNKS];
@@ -115,14 +115,12 @@ __global__ __launch_bounds__(256, 2) void proj_bf16_kernel(ProjArgs a) {
 #pragma unroll
         for (int j = 0; j < A_CHUNKS; ++j) {
             const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&a_lds[buf][row * BK + swz(row, akc) * 8]) =
-                aok[j] ? areg[R][j] : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(&a_lds[buf][row * BK + swz(row, akc) * 8]) = areg[R][j];
         }
 #pragma unroll
         for (int j = 0; j < B_CHUNKS; ++j) {
             const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&b_lds[buf][row * BK + swz(row, akc) * 8]) =
-                bok[j] ? breg[R][j] : u32x4{0, 0, 0, 0};
+            *reinterpret_cast<u32x4*>(&b_lds[buf][row * BK + swz(row, akc) * 8]) = breg[R][j];
         }
     };
 
