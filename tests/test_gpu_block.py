@@ -29,7 +29,9 @@ MID = si.Workload("block_mid", 2, 256, 32, 32, 4, 4, seed=5201)                 
 RAGGED = si.Workload("block_ragged", 1, 128, 20, 13, 4, 2, seed=5202)           # Lq = 65
 RAGGED_F32 = si.Workload("block_ragged_f32", 2, 128, 12, 7, 3, 2, groups=16, dtype="f32",
                          sigma=0.05, seed=5203)
-ASYNC_CASES = [(W["tiny"], 1), (MID, 2), (RAGGED, 3), (RAGGED_F32, 0), (W["sdxl1024_l2"], 5)]
+ONE_PATCH = si.Workload("block_n1", 1, 128, 8, 9, 1, 2, seed=5204)            # n = 1: no stale context
+ASYNC_CASES = [(W["tiny"], 1), (MID, 2), (RAGGED, 3), (RAGGED_F32, 0), (W["sdxl1024_l2"], 5),
+               (ONE_PATCH, 0)]
 
 
 def _ids(cases):
@@ -133,7 +135,7 @@ def test_block_async_step(wl, patch):
         assert torch.equal(_bits(st_same[k]), _bits(st_out[k])), k
 
 
-@pytest.mark.parametrize("wl", [MID, W["tiny"]], ids=["block_mid", "tiny"])
+@pytest.mark.parametrize("wl", [MID, W["tiny"], RAGGED_F32], ids=["block_mid", "tiny", "ragged_f32"])
 def test_block_warmup_then_async_step(wl):
     """Step 1 synchronous over all patches on the previous map, step 2
     asynchronous for patch i on the current map, against the oracle's own two
