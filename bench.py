@@ -252,7 +252,7 @@ def block_bench(levels, iters):
                           dtype=torch.uint8, device="cuda")
         cx_ms, _ = time_op(lambda i: dp.distri_patch_cross_attn(wl.geom, wl.heads, cx["q"], cx["k_ctx"],
                                                                 cx["v_ctx"], out=co, workspace=cws), iters)
-        cx_bytes = 2 * (cx["q"].numel() + 2 * cx["k_ctx"].numel())
+        cx_bytes = 2 * (2 * cx["q"].numel() + 2 * cx["k_ctx"].numel())  # Q, O, context K and V
         cx_fl = 4.0 * B * wl.heads * Lq * 77 * wl.head_dim
         del cx, co, cws
         ng = dp.naive_geom(wl.geom)

@@ -138,7 +138,10 @@ int distri_patch_cross_attn_workspace_size(const distri_patch_geom* g, int64_t h
     int st = check_cross_shape(g, heads, head_dim, ctx_len, dtype);
     if (st) return st;
     const dp::Geom gg = to_geom(g);
-    *bytes = dp::attention_workspace_bytes(gg.B, gg.lq(), ctx_len, heads, dtype == DISTRI_BF16);
+    const bool bf16 = dtype == DISTRI_BF16;
+    *bytes = bf16 && dp::cross_attention_short(gg.lq(), ctx_len, heads)
+                 ? 0
+                 : dp::attention_workspace_bytes(gg.B, gg.lq(), ctx_len, heads, bf16);
     return DISTRI_OK;
 }
 
@@ -160,17 +163,22 @@ int distri_patch_cross_attn(const distri_patch_geom* g, int64_t heads, int64_t h
     const Range o{out, local};
     DP_CHECK(!overlaps(o, {q, local}) && !overlaps(o, {k_ctx, ctx}) && !overlaps(o, {v_ctx, ctx}),
              DISTRI_ERR_ALIAS, "out overlaps an input");
-    const size_t need = dp::attention_workspace_bytes(gg.B, gg.lq(), ctx_len, heads,
-                                                      dtype == DISTRI_BF16);
+    const bool bf16 = dtype == DISTRI_BF16;
+    const bool short_ctx = bf16 && dp::cross_attention_short(gg.lq(), ctx_len, heads);
+    const size_t need =
+        short_ctx ? 0 : dp::attention_workspace_bytes(gg.B, gg.lq(), ctx_len, heads, bf16);
     if (need > 0) {
         DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
                  "attention workspace missing or too small");
         DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
         DP_CHECK(!overlaps({workspace, need}, o), DISTRI_ERR_ALIAS, "workspace overlaps out");
     }
+    if (short_ctx)  // the whole context held in LDS
+        return hip_status(dp::launch_cross_attention(gg.B, gg.lq(), ctx_len, heads, scale, q, k_ctx,
+                                                     v_ctx, out, static_cast<hipStream_t>(stream)));
     // every key is a context token: the fresh range starts past the context
     return hip_status(dp::launch_attention_rows(gg.B, gg.lq(), ctx_len, ctx_len, heads, scale,
-                                                dtype == DISTRI_BF16, q, k_ctx, v_ctx, k_ctx,
+                                                bf16, q, k_ctx, v_ctx, k_ctx,
                                                 v_ctx, out, workspace,
                                                 static_cast<hipStream_t>(stream)));
 }

@@ -111,6 +111,15 @@ hipError_t launch_attention_rows(int64_t B, int64_t lq, int64_t L, int64_t own_l
                                  const void* vf, const void* ks, const void* vs, void* out,
                                  void* ws, hipStream_t s);
 
+// Cross-attention over a context of at most kCrossCtxMax tokens, held in LDS
+// whole (bf16 only): q / out [B, lq, heads, 64], k / v [B, ctx, heads, 64].
+// No workspace.  cross_attention_short() says whether a shape takes it.
+constexpr int kCrossCtxMax = 128;
+bool cross_attention_short(int64_t lq, int64_t ctx, int64_t heads);
+hipError_t launch_cross_attention(int64_t B, int64_t lq, int64_t ctx, int64_t heads, float scale,
+                                  const void* q, const void* k, const void* v, void* out,
+                                  hipStream_t s);
+
 hipError_t launch_qkv_proj(const Geom& g, int64_t C, bool bf16, const void* x, const void* w_qkv,
                            const float* bias, void* q, void* k, void* v, void* k_stale,
                            void* v_stale, hipStream_t s);

@@ -119,8 +119,10 @@ int distri_patch_self_attn(const distri_patch_geom *g, int64_t heads, int64_t he
  *   q, out          [B, Lq, heads, head_dim]   dtype
  *   k_ctx, v_ctx    [B, ctx_len, heads, head_dim] dtype
  *   workspace       >= distri_patch_cross_attn_workspace_size() bytes
- * head_dim must be 64 and ctx_len >= 1; same kernels and limits as
- * distri_patch_self_attn, with L = ctx_len.
+ * head_dim must be 64 and ctx_len >= 1.  In bf16 with ctx_len <= 128 the
+ * whole context of one (image, head) is held on chip and the workspace size
+ * is 0; otherwise the self-attention kernels run with L = ctx_len, under the
+ * same limits as distri_patch_self_attn.
  */
 int distri_patch_cross_attn_workspace_size(const distri_patch_geom *g, int64_t heads,
                                            int64_t head_dim, int64_t ctx_len, int dtype,

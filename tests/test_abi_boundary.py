@@ -321,3 +321,8 @@ def test_cross_attention_rejects_bad_arguments(lib):
     n = ctypes.c_size_t(0)
     assert lib.distri_patch_cross_attn_workspace_size(G(*g), 10, 64, 77, BF16, ctypes.byref(n)) == OK
     assert lib.distri_patch_cross_attn_workspace_size(G(*g), 10, 64, 0, BF16, ctypes.byref(n)) == SHAPE
+    # bf16 contexts of at most 128 tokens are held on chip whole: no workspace
+    for ctx in (1, 77, 128):
+        n.value = 12345
+        assert lib.distri_patch_cross_attn_workspace_size(G(*g), 10, 64, ctx, BF16, ctypes.byref(n)) == OK
+        assert n.value == 0

@@ -23,8 +23,16 @@ def _gpu():
 
 W = si.WORKLOADS
 RAGGED = si.Workload("f4_ragged", 1, 128, 20, 13, 4, 2, seed=5301)     # Lq = 65
+RAGGED2 = si.Workload("f4_ragged2", 2, 192, 12, 9, 2, 3, seed=5302)    # Lq = 54, 2 images, 3 heads
+# 40 (image, head) pairs x 96 query blocks: the short-context kernel runs
+# several query blocks per wave (the next block's Q loaded during this one)
+MANY = si.Workload("f4_many_blocks", 2, 1280, 64, 48, 1, 20, seed=5303)  # Lq = 3072
+# bf16 contexts of at most 128 tokens take the kernel that holds the whole
+# context on chip (1..4 blocks of 32 keys, partial last block); longer ones
+# and fp32 take the self-attention kernels
 CROSS_CASES = [(W["tiny"], 0, 77), (W["sdxl1024_l2"], 3, 77), (W["sdxl1024_l3"], 1, 77),
-               (RAGGED, 2, 5), (RAGGED, 1, 1), (RAGGED, 3, 300)]
+               (RAGGED, 2, 5), (RAGGED, 1, 1), (RAGGED, 3, 300), (RAGGED, 0, 32), (RAGGED2, 1, 96),
+               (RAGGED2, 0, 17), (W["sdxl1024_l2"], 6, 128), (RAGGED, 1, 129), (MANY, 0, 77)]
 
 
 @pytest.mark.parametrize("wl,patch,ctx", CROSS_CASES,
