@@ -12,19 +12,25 @@
 // is loaded.
 //
 // bf16 kernel (gfx950, bf16 MFMA, fp32 accumulation):
-//  * block = 4 waves x 64 queries (a 256-query tile of one image and head);
-//    every wave keeps its Q^T fragments in registers for the whole key loop;
-//  * work plan: with P = 2 blocks per CU running at once, whole (tile, head,
-//    image) tasks are handed out in full rounds of P blocks; the tasks left
-//    over are split along the keys into S chunks (S from a small cost model)
-//    so the last round also fills the machine, and a combine kernel merges
-//    the chunks' partial (O, max, sum).  Block ids are remapped so that the
-//    blocks one XCD runs at the same time hold neighbouring tiles of the same
-//    head and walk the same keys together, sharing K/V tiles in that XCD's L2;
-//  * key tiles of 64 rows are staged in LDS, double-buffered: K row-major
-//    (MFMA A operand for S^T = K Q^T) and V transposed to V^T[d][key] while it
-//    is written (A operand for O^T = V^T P^T), so every MFMA operand is a
-//    plain ds_read;
+//  * block = 8 waves x 64 queries (a 512-query tile of one image and head),
+//    one block per CU; every wave keeps its Q^T fragments in registers for
+//    the whole key loop;
+//  * work plan: with P = one block per CU running at once, whole (tile,
+//    head, image) tasks are handed out in full rounds of P blocks; the tasks
+//    left over are split along the keys into S chunks (S from a small cost
+//    model) so the last round also fills the machine, and a combine kernel
+//    merges the chunks' partial (O, max, sum).  Block ids are remapped so
+//    that the blocks one XCD runs at the same time hold neighbouring tiles of
+//    the same head and walk the same keys together, sharing K/V tiles in that
+//    XCD's L2;
+//  * key tiles of 64 rows go from global memory straight into LDS
+//    (global_load_lds_dwordx4: no registers, no LDS store instructions) in
+//    three stages, the loads two tiles ahead of their use.  K and V are
+//    both kept row-major, each row's 16-byte granules XOR-swizzled so that
+//    the operand reads hit every LDS bank evenly: K rows are the MFMA A
+//    operand of S^T = K Q^T (ds_read_b128), and the V^T operand of O^T =
+//    V^T P^T comes from the transposing read ds_read_b64_tr_b16 (a 16-lane
+//    group turns 16 4-element row pieces into 4-key columns);
 //  * S is computed transposed (keys x queries) with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 keys of ONE query per 32x32 block, so the row max and
 //    row sum are in-lane reductions plus one exchange between the two
@@ -56,13 +62,29 @@ namespace {
 
 constexpr int D = 64;        // head dim
 constexpr int KT = 64;       // keys per tile
-constexpr int NWAVES = 4;    // waves per block
+constexpr int NWAVES = 8;    // waves per block
 constexpr int QB = 2;        // 32-query blocks per wave
 constexpr int QTILE = NWAVES * QB * 32;
-constexpr int KPITCH = D + 8;   // LDS row pitch of K (bf16 elements)
-constexpr int VPITCH = KT + 4;  // LDS row pitch of V^T (bf16 elements)
+constexpr int NSTAGE = 3;       // K/V tile stages in LDS (loads run two tiles ahead)
 constexpr int kPartialCost = 3; // cost of one partial write + merge, in key tiles
 constexpr float kSumLimit = 4096.0f;  // largest lane sum of P kept without moving the max
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+#define DP_LDS __attribute__((address_space(3)))
+// s_waitcnt immediates (gfx9 encoding, expcnt and lgkmcnt left free)
+constexpr int kVmcnt0 = 0x0F70;
+constexpr int kVmcnt2 = 0x0F72;
+
+// byte address in LDS of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const DP_LDS void*)(p)));
+}
+// 16-byte granule swizzles of a K and a V tile row.  K: the 32 rows of an
+// operand read spread over all eight granule positions; V: the eight rows
+// of a transposing read land on both halves of the granule range.
+__device__ __forceinline__ int k_swizzle(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int v_swizzle(int row) { return ((row >> 1) & 1) * 4; }
 
 // Work plan shared by the host launcher and both kernels.
 struct Plan {
@@ -98,7 +120,7 @@ Plan make_plan(int64_t B, int64_t heads, int64_t lq, int64_t L, int cus) {
     p.nqt = int(ceil_div(lq, QTILE));
     p.nkt = int(ceil_div(L, KT));
     p.tasks = B * heads * p.nqt;
-    p.P = 2 * (cus > 4 ? cus : 4);
+    p.P = cus > 8 ? cus : 8;  // one block of 8 waves per CU
     p.P -= p.P % 8;
     p.F = (p.tasks / p.P) * p.P;
     p.R = int(p.tasks - p.F);
@@ -126,9 +148,10 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
     return (w % 8) * (n8 / 8) + w / 8;
 }
 
-__global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][KT * KPITCH];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][D * VPITCH];
+__global__ __launch_bounds__(NWAVES * 64, 1) void attn_bf16_kernel(AttnArgs a) {
+    // NSTAGE stages of [K tile | V tile], each 64 rows x 128 bytes, row t's
+    // 16-byte granule c stored at position c ^ swizzle(t)
+    __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NSTAGE][2][KT * D];
     const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
     const Plan& pl = a.plan;
 
@@ -170,67 +193,59 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
         for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
     }
 
-    // tile-load mapping: K rows kk and kk+32, V rows 2kk and 2kk+1, 8 dims each.
-    // A token row comes from the fresh slice inside the patch, else from the
-    // stale map (32-bit offsets: the ABI bounds L * heads * D below 2^31).
-    // Tiles wholly on one side of the patch boundary (all but at most two)
-    // take one wave-uniform base pointer; a straddling tile selects per row.
+    // Tile loads: thread tid loads 16 bytes of K and of V from token row
+    // kt*64 + (tid >> 3) of the tile; its lane slot in LDS is granule
+    // tid & 7 of that row, so it reads the granule that the row's swizzle
+    // puts there.  A token row comes from the fresh slice inside the patch,
+    // else from the stale map (32-bit offsets: the ABI bounds L * heads * D
+    // below 2^31); rows past the map are clamped to its last row, whose keys
+    // the last tile masks.  The loads are written in asm: the compiler would
+    // otherwise wait for every load into LDS before any LDS read, which
+    // serialises the pipeline; their completion is the explicit vmcnt wait
+    // at the top of each tile instead.  They have no register results.
     const int c8 = tid & 7;
-    const int kk = tid >> 3;
+    const int krow = tid >> 3;
     const uint16_t* kst = a.ks + (b * a.L * a.heads + hd) * D;
     const uint16_t* vst = a.vs + (b * a.L * a.heads + hd) * D;
     const uint16_t* kfr = a.kf + (b * a.lq * a.heads + hd) * D;
     const uint16_t* vfr = a.vf + (b * a.lq * a.heads + hd) * D;
-    const int roff[4] = {kk * rs + c8 * 8, (kk + 32) * rs + c8 * 8, 2 * kk * rs + c8 * 8,
-                         (2 * kk + 1) * rs + c8 * 8};
-    const int rkey[4] = {kk, kk + 32, 2 * kk, 2 * kk + 1};
-    u32x4 kr[2], vr[2];
-    auto gload = [&](int kt) {
-        const int t0 = kt * KT;
-        const int own_hi = a.own_lo + a.lq;
-        if (t0 + KT <= a.L && (t0 + KT <= a.own_lo || t0 >= own_hi)) {
-            const uint16_t* kb0 = kst + t0 * rs;
-            const uint16_t* vb0 = vst + t0 * rs;
-            kr[0] = *reinterpret_cast<const u32x4*>(kb0 + roff[0]);
-            kr[1] = *reinterpret_cast<const u32x4*>(kb0 + roff[1]);
-            vr[0] = *reinterpret_cast<const u32x4*>(vb0 + roff[2]);
-            vr[1] = *reinterpret_cast<const u32x4*>(vb0 + roff[3]);
-        } else if (t0 >= a.own_lo && t0 + KT <= own_hi) {
-            const uint16_t* kb0 = kfr + (t0 - a.own_lo) * rs;
-            const uint16_t* vb0 = vfr + (t0 - a.own_lo) * rs;
-            kr[0] = *reinterpret_cast<const u32x4*>(kb0 + roff[0]);
-            kr[1] = *reinterpret_cast<const u32x4*>(kb0 + roff[1]);
-            vr[0] = *reinterpret_cast<const u32x4*>(vb0 + roff[2]);
-            vr[1] = *reinterpret_cast<const u32x4*>(vb0 + roff[3]);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = t0 + rkey[j];
-                const int rel = t - a.own_lo;
-                const bool fresh = unsigned(rel) < unsigned(a.lq);
-                const uint16_t* base = j < 2 ? (fresh ? kfr : kst) : (fresh ? vfr : vst);
-                const int off = (fresh ? rel : t) * rs + c8 * 8;
-                const u32x4 v = t < a.L ? *reinterpret_cast<const u32x4*>(base + off) : u32x4{0, 0, 0, 0};
-                if (j < 2)
-                    kr[j] = v;
-                else
-                    vr[j - 2] = v;
-            }
-        }
+    const int kgran = (c8 ^ k_swizzle(krow)) * 8;
+    const int vgran = (c8 ^ v_swizzle(krow)) * 8;
+    const uint32_t slot = uint32_t(wave * 64) * 16;
+    auto tile_load = [&](int kt, int stage) {
+        int t = kt * KT + krow;
+        if (t > a.L - 1) t = a.L - 1;
+        const int rel = t - a.own_lo;
+        const bool fresh = unsigned(rel) < unsigned(a.lq);
+        const int off = (fresh ? rel : t) * rs;
+        const uint16_t* kp = (fresh ? kfr : kst) + off + kgran;
+        const uint16_t* vp = (fresh ? vfr : vst) + off + vgran;
+        const uint32_t m0k = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][0][0]) + slot);
+        const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][1][0]) + slot);
+        // (m0 is written inside each asm statement; this kernel keeps
+        // nothing else in m0, a register the compiler reserves)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(kp), "s"(m0k) : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vp), "s"(m0v) : "memory", "m0");
+#pragma clang diagnostic pop
     };
-    auto lstore = [&](int buf) {
+    // K operand (row kb*32 + lr, dims ks*16 + g*8 ..): granule 2 ks + g of
+    // the row, swizzled; the row's swizzle depends on lr only
+    const int ksw = k_swizzle(lr);
+    // V^T operand by transposing read: within each 16-lane group (i = lane
+    // & 15) lane i hands over the 4 dims (16 ((lane >> 4) & 1) + 4 (i & 3))..
+    // of key row 4g + (i >> 2) of an 8-key run and receives dim
+    // 16 ((lane >> 4) & 1) + i of keys 4g .. 4g + 3: the lane's MFMA row
+    // db*32 + lr.  vlane[db]: its byte address within the run.
+    const int ti = lane & 15;
+    const int vrow = 4 * g + (ti >> 2);
+    uint32_t vlane[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            *reinterpret_cast<u32x4*>(&k_lds[buf][(kk + 32 * j) * KPITCH + c8 * 8]) = kr[j];
-        // V^T[d][key]: pack (V[2kk][d], V[2kk+1][d]) into one dword per d
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = __builtin_amdgcn_perm(vr[1][j], vr[0][j], 0x05040100u);
-            const uint32_t hi = __builtin_amdgcn_perm(vr[1][j], vr[0][j], 0x07060302u);
-            *reinterpret_cast<uint32_t*>(&v_lds[buf][(c8 * 8 + 2 * j) * VPITCH + 2 * kk]) = lo;
-            *reinterpret_cast<uint32_t*>(&v_lds[buf][(c8 * 8 + 2 * j + 1) * VPITCH + 2 * kk]) = hi;
-        }
-    };
+    for (int db = 0; db < 2; ++db) {
+        const int gran = (db * 4 + 2 * ((lane >> 4) & 1) + ((ti & 3) >> 1)) ^ v_swizzle(vrow);
+        vlane[db] = uint32_t(vrow * 128 + gran * 16 + (ti & 1) * 8);
+    }
 
     f32x16 o[2][QB];
 #pragma unroll
@@ -249,8 +264,8 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // kMask (a std::integral_constant) masks keys past the end of the map;
     // only the map's last, partial tile needs it.
     // A wave whose 64 queries all lie past the patch (the last query tile of
-    // a map whose Lq is not a multiple of 256) only loads and syncs, which
-    // leaves its SIMD to the other block on the CU.
+    // a map whose Lq is not a multiple of 512) only loads and syncs, which
+    // leaves its SIMD to the wave of the block that shares it.
     const bool wave_active = q0 < a.lq;
     // S^T = K Q^T of LDS stage `cur` for query blocks qb in [q_lo, q_hi):
     // s[kb][qb] covers keys kb*32.. and queries qb*32..; keys past the map
@@ -261,7 +276,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const bf16x8 ka = *reinterpret_cast<const bf16x8*>(
-                    &k_lds[cur][(kb * 32 + lr) * KPITCH + ks * 16 + g * 8]);
+                    &kv_lds[cur][0][(kb * 32 + lr) * D + (((2 * ks + g) ^ ksw) * 8)]);
 #pragma unroll
                 for (int qb = q_lo; qb < q_hi; ++qb)
                     s[kb][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
@@ -315,11 +330,20 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
     // in LDS.  kMask (a std::integral_constant) masks keys past the end of
     // the map; only the map's last, partial tile needs it.
     // A wave whose 64 queries all lie past the patch (the last query tile of
-    // a map whose Lq is not a multiple of 256) only loads and syncs, which
-    // leaves its SIMD to the other block on the CU.
+    // a map whose Lq is not a multiple of 512) only loads and syncs, which
+    // leaves its SIMD to the wave of the block that shares it.
     auto tile = [&](int kt, auto kMask) {
-        const int cur = (kt - kt0) & 1;
-        if (kt + 1 < kt1) gload(kt + 1);
+        const int cur = (kt - kt0) % NSTAGE;
+        // this thread's loads of tile kt are done (those of tile kt + 1, two
+        // per thread, may still be in flight); after the barrier every
+        // wave's share is in LDS and every wave has left tile kt - 1, whose
+        // stage the loads of tile kt + 2 then take
+        if (kt + 1 < kt1)
+            __builtin_amdgcn_s_waitcnt(kVmcnt2);
+        else
+            __builtin_amdgcn_s_waitcnt(kVmcnt0);
+        __syncthreads();
+        if (kt + 2 < kt1) tile_load(kt + 2, (kt + 2 - kt0) % NSTAGE);
         if (wave_active) {
             f32x16 s[2][QB];
             // one query block after the other, so that the second block's
@@ -369,11 +393,13 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                     for (int h2 = 0; h2 < 2; ++h2) {
 #pragma unroll
                         for (int db = 0; db < 2; ++db) {
-                            const uint16_t* vp =
-                                &v_lds[cur][(db * 32 + lr) * VPITCH + kb * 32 + h2 * 16 + 4 * g];
-                            const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vp);
-                            const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vp + 8);
-                            const bf16x8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            const uint32_t vb =
+                                lds_addr(&kv_lds[cur][1][0]) + vlane[db] + (kb * 32 + h2 * 16) * 128;
+                            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DP_LDS i16x4*)(vb));
+                            const i16x4 hi =
+                                __builtin_amdgcn_ds_read_tr16_b64_v4i16((DP_LDS i16x4*)(vb + 8 * 128));
+                            const bf16x8 va = __builtin_bit_cast(
+                                bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
                             o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kb][h2], o[db][qb],
                                                                                 0, 0, 0);
                         }
@@ -381,13 +407,14 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
                 }
             }
         }
-        if (kt + 1 < kt1) lstore(cur ^ 1);
-        __syncthreads();
     };
 
-    gload(kt0);
-    lstore(0);
-    __syncthreads();
+    // Q is in registers before the first tile load is issued, so that the
+    // compiler has no load of its own in flight inside the key loop (its
+    // wait for one would also wait for the tile loads)
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    tile_load(kt0, 0);
+    if (kt0 + 1 < kt1) tile_load(kt0 + 1, 1);
     const int full_end = (kt1 == pl.nkt && a.L % KT != 0) ? kt1 - 1 : kt1;
     for (int kt = kt0; kt < full_end; ++kt) tile(kt, std::false_type{});
     if (full_end < kt1) tile(full_end, std::true_type{});
@@ -438,7 +465,7 @@ __global__ __launch_bounds__(256, 2) void attn_bf16_kernel(AttnArgs a) {
 // the rows and S * 8 loads per thread stay in flight together.
 constexpr int kCombineDims = 8;
 
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(QTILE) void attn_combine_kernel(AttnArgs a) {
     const Plan& pl = a.plan;
     const int r = blockIdx.x;
     const int d0 = blockIdx.y * kCombineDims;
@@ -589,7 +616,7 @@ hipError_t launch_attention_rows(int64_t B, int64_t lq, int64_t L, int64_t own_l
         a.own_lo = int(own_lo);
         a.heads = int(heads);
         a.c = scale * 1.4426950408889634f;
-        hipLaunchKernelGGL(attn_bf16_kernel, dim3(unsigned(a.plan.grid())), dim3(256), 0, s, a);
+        hipLaunchKernelGGL(attn_bf16_kernel, dim3(unsigned(a.plan.grid())), dim3(NWAVES * 64), 0, s, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess || a.plan.partials() == 0) return e;
         hipLaunchKernelGGL(attn_combine_kernel, dim3(unsigned(a.plan.R), D / kCombineDims), dim3(QTILE),
