@@ -94,7 +94,22 @@ struct Plan {
     int64_t F;      // tasks run whole, in full rounds of P blocks
     int R;          // tasks left over, each split into S key chunks
     int S;
+    int nfull;      // query tiles per (image, head) that hold QTILE queries
     int64_t grid() const { return F + int64_t(R) * S; }
+    // Task order: every (image, head)'s full query tiles first, head after
+    // head, then the partial last tiles of all heads.  The partial tiles (one
+    // wave of queries at level a) thus fall into the key-split remainder
+    // instead of taking a CU for a whole round of full tasks.
+    __host__ __device__ void tile_of(int64_t task, int64_t& bh, int& qt) const {
+        const int64_t nf = tasks / nqt * nfull;  // tasks on full tiles
+        if (task < nf) {
+            bh = task / nfull;
+            qt = int(task % nfull);
+        } else {
+            bh = task - nf;
+            qt = nqt - 1;
+        }
+    }
     int64_t partials() const { return S > 1 ? int64_t(R) * S : 0; }
 };
 
@@ -118,6 +133,7 @@ struct AttnArgs {
 Plan make_plan(int64_t B, int64_t heads, int64_t lq, int64_t L, int cus) {
     Plan p;
     p.nqt = int(ceil_div(lq, QTILE));
+    p.nfull = int(lq / QTILE);
     p.nkt = int(ceil_div(L, KT));
     p.tasks = B * heads * p.nqt;
     p.P = cus > 8 ? cus : 8;  // one block of 8 waves per CU
@@ -171,8 +187,9 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         kt1 = int(int64_t(c + 1) * pl.nkt / pl.S);
         if (pl.S > 1) part = int64_t(r) * pl.S + c;
     }
-    const int64_t bh = task / pl.nqt;
-    const int qt = int(task % pl.nqt);
+    int64_t bh;
+    int qt;
+    pl.tile_of(task, bh, qt);
     const int64_t b = bh / a.heads, hd = bh % a.heads;
 
     const int tid = threadIdx.x;
@@ -470,8 +487,9 @@ __global__ __launch_bounds__(QTILE) void attn_combine_kernel(AttnArgs a) {
     const int r = blockIdx.x;
     const int d0 = blockIdx.y * kCombineDims;
     const int64_t task = pl.F + r;
-    const int64_t bh = task / pl.nqt;
-    const int qt = int(task % pl.nqt);
+    int64_t bh;
+    int qt;
+    pl.tile_of(task, bh, qt);
     const int64_t b = bh / a.heads, hd = bh % a.heads;
     const int row = threadIdx.x;
     const int qrow = qt * QTILE + row;
