@@ -62,7 +62,9 @@ namespace {
 
 constexpr int D = 64;        // head dim
 constexpr int KT = 64;       // keys per tile
-constexpr int NWAVES = 8;    // waves per block
+constexpr int NWAVES = 8;    // waves per block (4 or 8)
+constexpr int BLOCKS_PER_CU = 8 / NWAVES;  // two waves per SIMD either way
+constexpr int TROWS = KT * 8 / (NWAVES * 64);  // K (and V) tile rows one thread loads
 constexpr int QB = 2;        // 32-query blocks per wave
 constexpr int QTILE = NWAVES * QB * 32;
 constexpr int NSTAGE = 3;       // K/V tile stages in LDS (loads run two tiles ahead)
@@ -74,7 +76,7 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 #define DP_LDS __attribute__((address_space(3)))
 // s_waitcnt immediates (gfx9 encoding, expcnt and lgkmcnt left free)
 constexpr int kVmcnt0 = 0x0F70;
-constexpr int kVmcnt2 = 0x0F72;
+constexpr int kVmcntTile = 0x0F70 + 2 * TROWS;  // vmcnt(one tile's loads per thread)
 
 // byte address in LDS of a __shared__ object
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -136,7 +138,7 @@ Plan make_plan(int64_t B, int64_t heads, int64_t lq, int64_t L, int cus) {
     p.nfull = int(lq / QTILE);
     p.nkt = int(ceil_div(L, KT));
     p.tasks = B * heads * p.nqt;
-    p.P = cus > 8 ? cus : 8;  // one block of 8 waves per CU
+    p.P = BLOCKS_PER_CU * (cus > 4 ? cus : 4);
     p.P -= p.P % 8;
     p.F = (p.tasks / p.P) * p.P;
     p.R = int(p.tasks - p.F);
@@ -164,7 +166,7 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
     return (w % 8) * (n8 / 8) + w / 8;
 }
 
-__global__ __launch_bounds__(NWAVES * 64, 1) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(AttnArgs a) {
     // NSTAGE stages of [K tile | V tile], each 64 rows x 128 bytes, row t's
     // 16-byte granule c stored at position c ^ swizzle(t)
     __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NSTAGE][2][KT * D];
@@ -210,10 +212,10 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_bf16_kernel(AttnArgs a) {
         for (int ks = 0; ks < 4; ++ks) qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qp + ks * 16);
     }
 
-    // Tile loads: thread tid loads 16 bytes of K and of V from token row
-    // kt*64 + (tid >> 3) of the tile; its lane slot in LDS is granule
-    // tid & 7 of that row, so it reads the granule that the row's swizzle
-    // puts there.  A token row comes from the fresh slice inside the patch,
+    // Tile loads: thread tid loads 16 bytes of K and of V from token rows
+    // kt*64 + (tid >> 3) + j * NWAVES * 8 (j < TROWS) of the tile; its lane
+    // slot in LDS is granule tid & 7 of that row, so it reads the granule
+    // that the row's swizzle puts there.  A token row comes from the fresh slice inside the patch,
     // else from the stale map (32-bit offsets: the ABI bounds L * heads * D
     // below 2^31); rows past the map are clamped to its last row, whose keys
     // the last tile masks.  The loads are written in asm: the compiler would
@@ -221,31 +223,32 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     // serialises the pipeline; their completion is the explicit vmcnt wait
     // at the top of each tile instead.  They have no register results.
     const int c8 = tid & 7;
-    const int krow = tid >> 3;
     const uint16_t* kst = a.ks + (b * a.L * a.heads + hd) * D;
     const uint16_t* vst = a.vs + (b * a.L * a.heads + hd) * D;
     const uint16_t* kfr = a.kf + (b * a.lq * a.heads + hd) * D;
     const uint16_t* vfr = a.vf + (b * a.lq * a.heads + hd) * D;
-    const int kgran = (c8 ^ k_swizzle(krow)) * 8;
-    const int vgran = (c8 ^ v_swizzle(krow)) * 8;
-    const uint32_t slot = uint32_t(wave * 64) * 16;
     auto tile_load = [&](int kt, int stage) {
-        int t = kt * KT + krow;
-        if (t > a.L - 1) t = a.L - 1;
-        const int rel = t - a.own_lo;
-        const bool fresh = unsigned(rel) < unsigned(a.lq);
-        const int off = (fresh ? rel : t) * rs;
-        const uint16_t* kp = (fresh ? kfr : kst) + off + kgran;
-        const uint16_t* vp = (fresh ? vfr : vst) + off + vgran;
-        const uint32_t m0k = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][0][0]) + slot);
-        const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][1][0]) + slot);
-        // (m0 is written inside each asm statement; this kernel keeps
-        // nothing else in m0, a register the compiler reserves)
+#pragma unroll
+        for (int j = 0; j < TROWS; ++j) {
+            const int krow = (tid >> 3) + j * NWAVES * 8;
+            int t = kt * KT + krow;
+            if (t > a.L - 1) t = a.L - 1;
+            const int rel = t - a.own_lo;
+            const bool fresh = unsigned(rel) < unsigned(a.lq);
+            const int off = (fresh ? rel : t) * rs;
+            const uint16_t* kp = (fresh ? kfr : kst) + off + (c8 ^ k_swizzle(krow)) * 8;
+            const uint16_t* vp = (fresh ? vfr : vst) + off + (c8 ^ v_swizzle(krow)) * 8;
+            const uint32_t slot = uint32_t(j * NWAVES * 64 + wave * 64) * 16;
+            const uint32_t m0k = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][0][0]) + slot);
+            const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][1][0]) + slot);
+            // (m0 is written inside each asm statement; this kernel keeps
+            // nothing else in m0, a register the compiler reserves)
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(kp), "s"(m0k) : "memory", "m0");
-        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vp), "s"(m0v) : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(kp), "s"(m0k) : "memory", "m0");
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vp), "s"(m0v) : "memory", "m0");
 #pragma clang diagnostic pop
+        }
     };
     // K operand (row kb*32 + lr, dims ks*16 + g*8 ..): granule 2 ks + g of
     // the row, swizzled; the row's swizzle depends on lr only
@@ -351,12 +354,12 @@ __global__ __launch_bounds__(NWAVES * 64, 1) void attn_bf16_kernel(AttnArgs a) {
     // leaves its SIMD to the wave of the block that shares it.
     auto tile = [&](int kt, auto kMask) {
         const int cur = (kt - kt0) % NSTAGE;
-        // this thread's loads of tile kt are done (those of tile kt + 1, two
-        // per thread, may still be in flight); after the barrier every
+        // this thread's loads of tile kt are done (those of tile kt + 1,
+        // 2 TROWS per thread, may still be in flight); after the barrier every
         // wave's share is in LDS and every wave has left tile kt - 1, whose
         // stage the loads of tile kt + 2 then take
         if (kt + 1 < kt1)
-            __builtin_amdgcn_s_waitcnt(kVmcnt2);
+            __builtin_amdgcn_s_waitcnt(kVmcntTile);
         else
             __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();

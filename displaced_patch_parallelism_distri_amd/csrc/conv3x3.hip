@@ -23,17 +23,18 @@
 //    three row sources are re-selected only when the tap changes.
 //  * The weight tile comes from [Cout][3][3][Cin], already K-contiguous per
 //    output channel.
-//  * Both tiles go global -> registers -> LDS, double-buffered: the loads of
-//    step s+1 are in flight while step s computes; one barrier per step.
-//    LDS rows are 128 bytes with the 16-byte chunks XOR-swizzled by
-//    (row / 2) % 8, which keeps the ds_read_b128 operand reads and the
-//    stores free of bank conflicts without padding (2 x 72 KB fit per CU).
+//  * Both tiles go from global memory straight into LDS
+//    (global_load_lds_dwordx4: no registers, no LDS store instructions),
+//    double-buffered: the loads of step s+1 are in flight while step s
+//    computes; one wait and one barrier per step.  LDS rows are 128 bytes
+//    with the 16-byte chunks XOR-swizzled by (row / 2) % 8, which keeps the
+//    ds_read_b128 operand reads free of bank conflicts without padding
+//    (2 x 72 KB fit per CU); a load's LDS slot is fixed by its lane, so each
+//    thread reads the logical chunk that the swizzle puts in its slot.
 //  * Blocks are remapped so that each XCD works through the tiles of one or
 //    two cout slices: their weights stay in that XCD's L2.
 // fp32 kernel: one thread per output element, direct sum; parity-grade.
 #include "dp_common.h"
-
-#include <type_traits>
 
 namespace dp {
 namespace {
@@ -59,6 +60,14 @@ struct ConvArgs {
     int cin, cout;
     int mtiles, ntiles;
 };
+
+#define DP_LDS __attribute__((address_space(3)))
+// byte address in LDS of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const DP_LDS void*)(p)));
+}
+// s_waitcnt immediate for vmcnt(0) (gfx9 encoding, expcnt and lgkmcnt free)
+constexpr int kVmcnt0 = 0x0F70;
 
 // 16-byte chunk position of chunk `c` of LDS row `r`
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
@@ -133,36 +142,42 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
 
     const int kchunks = a.cin / BK;
     const int nsteps = 9 * kchunks;
-    // Two register sets: the loads of step s + 2 are issued while step s
-    // computes, and step s + 1's values (loaded a step earlier) are stored to
-    // LDS at the end of step s.  Padding rows already read zeros and weight
-    // rows past Cout read row 0's weights (they feed only output columns that
-    // are never stored), so the values go to LDS as loaded.
-    u32x4 areg[2][A_CHUNKS], breg[2][B_CHUNKS];
-    auto gload = [&](int s, auto set) {
-        constexpr int R = decltype(set)::value;
+    // Tile loads straight into LDS: instruction j of wave w writes LDS
+    // granules j*256 + w*64 + lane, i.e. row (tid >> 3) + 32 j at physical
+    // chunk tid & 7, so the thread reads the logical chunk stored there.
+    // Padding rows read zeros and weight rows past Cout read row 0 (they
+    // feed only output columns that are never stored).  The loads are
+    // inline asm with no register results: the compiler would otherwise
+    // wait for every load into LDS before any LDS read; their completion is
+    // the explicit wait at the top of each step.  m0 is written inside each
+    // asm statement; this kernel keeps nothing else in m0.
+    int alc[A_CHUNKS], blc[B_CHUNKS];
+#pragma unroll
+    for (int j = 0; j < A_CHUNKS; ++j) alc[j] = swz((tid >> 3) + 32 * j, akc) * 8;
+#pragma unroll
+    for (int j = 0; j < B_CHUNKS; ++j) blc[j] = swz((tid >> 3) + 32 * j, akc) * 8 - akc * 8;
+    const uint32_t wslot = uint32_t(wave) * 64 * 16;
+    auto tile_load = [&](int s, int buf) {
         const int tap = s / kchunks;
         const int ci0 = (s - tap * kchunks) * BK;
         if (ci0 == 0) set_tap(tap);
-#pragma unroll
-        for (int j = 0; j < A_CHUNKS; ++j)
-            areg[R][j] = *reinterpret_cast<const u32x4*>(aptr[j] + ci0 + akc * 8);
-#pragma unroll
-        for (int j = 0; j < B_CHUNKS; ++j)
-            breg[R][j] = *reinterpret_cast<const u32x4*>(bptr[j] + tap * a.cin + ci0);
-    };
-    auto lstore = [&](int buf, auto set) {
-        constexpr int R = decltype(set)::value;
+        const uint32_t al = lds_addr(&a_lds[buf][0]) + wslot;
+        const uint32_t bl = lds_addr(&b_lds[buf][0]) + wslot;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
         for (int j = 0; j < A_CHUNKS; ++j) {
-            const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&a_lds[buf][row * BK + swz(row, akc) * 8]) = areg[R][j];
+            const uint16_t* p = aptr[j] + ci0 + alc[j];
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(al + j * 256 * 16);
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(m0) : "memory", "m0");
         }
 #pragma unroll
         for (int j = 0; j < B_CHUNKS; ++j) {
-            const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&b_lds[buf][row * BK + swz(row, akc) * 8]) = breg[R][j];
+            const uint16_t* p = bptr[j] + tap * a.cin + ci0 + blc[j];
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(bl + j * 256 * 16);
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(m0) : "memory", "m0");
         }
+#pragma clang diagnostic pop
     };
 
     f32x4 acc[MT][NT];
@@ -192,25 +207,17 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
     };
-    // step s computes LDS buffer s % 2 from register set s % 2's data
-    auto step = [&](int s, auto set) {
-        constexpr int R = decltype(set)::value;
-        constexpr int Rn = R ^ 1;
-        if (s + 2 < nsteps) gload(s + 2, set);
-        compute(R);
-        if (s + 1 < nsteps) lstore(Rn, std::integral_constant<int, Rn>());
+    // step s: its loads are done, then the barrier (every wave's share is
+    // in LDS and every wave has left step s - 1, whose buffer the loads of
+    // step s + 1 then take), then compute.  Nothing of the compiler's own
+    // is in flight when the first load is issued.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    tile_load(0, 0);
+    for (int s = 0; s < nsteps; ++s) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
-    };
-
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    gload(0, S0());
-    if (nsteps > 1) gload(1, S1());
-    lstore(0, S0());
-    __syncthreads();
-    for (int s = 0; s < nsteps; s += 2) {
-        step(s, S0());
-        if (s + 1 < nsteps) step(s + 1, S1());
+        if (s + 1 < nsteps) tile_load(s + 1, (s + 1) & 1);
+        compute(s & 1);
     }
 
     // epilogue: acc[i][j][e] is pixel m0 + wm*WM + i*16 + 4*lq + e,

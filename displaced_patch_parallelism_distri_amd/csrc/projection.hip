@@ -16,12 +16,10 @@
 // bf16 kernel: a GEMM on v_mfma_f32_16x16x32_bf16 with the structure of the
 // conv kernel - a BM x 160 block tile, 4 waves in a 2 x 2 grid of
 // (BM/2) x 80 wave tiles, 64-wide K steps through swizzled double-buffered
-// LDS with two register sets of prefetch - minus the halo gather: A rows are
-// contiguous token rows.
+// LDS filled by direct global -> LDS loads one step ahead - minus the halo
+// gather: A rows are contiguous token rows.
 // fp32 kernel: one thread per output element, direct sum; parity-grade.
 #include "dp_common.h"
-
-#include <type_traits>
 
 namespace dp {
 namespace {
@@ -53,6 +51,14 @@ struct ProjArgs {
 
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+#define DP_LDS __attribute__((address_space(3)))
+// byte address in LDS of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const DP_LDS void*)(p)));
+}
+// s_waitcnt immediate for vmcnt(0) (gfx9 encoding, expcnt and lgkmcnt free)
+constexpr int kVmcnt0 = 0x0F70;
+
 template <int BM>
 __global__ __launch_bounds__(256, 2) void proj_bf16_kernel(ProjArgs a) {
     constexpr int WM = BM / 2, MT = WM / 16;
@@ -79,49 +85,51 @@ __global__ __launch_bounds__(256, 2) void proj_bf16_kernel(ProjArgs a) {
     const int nt = logical / a.mtiles, mt = logical % a.mtiles;
     const int m0 = mt * BM, n0 = nt * BN;
 
-    // loaders: chunk c = tid + 256 j -> row c / 8, 16-byte chunk c % 8; rows
-    // past M / N re-read row 0: they feed only outputs that are never stored
+    // Tile loads straight into LDS (global_load_lds_dwordx4): instruction j
+    // of wave w writes LDS granules j*256 + w*64 + lane, i.e. row
+    // (tid >> 3) + 32 j at physical chunk tid & 7, so the thread reads the
+    // logical chunk the row's swizzle stores there.  Rows past M / N re-read
+    // row 0: they feed only outputs that are never stored.  The loads are
+    // inline asm with no register results (the compiler would otherwise
+    // wait for every load into LDS before any LDS read); their completion
+    // is the explicit wait at the top of each step.  m0 is written inside
+    // each asm statement; this kernel keeps nothing else in m0.
     const int akc = tid & 7;
     const uint16_t* aptr[A_CHUNKS];
-    bool aok[A_CHUNKS];
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) {
-        const int m = m0 + (tid >> 3) + 32 * j;
-        aok[j] = m < a.M;
-        aptr[j] = a.x + size_t(aok[j] ? m : 0) * a.K + akc * 8;
+        const int row = (tid >> 3) + 32 * j;
+        const int m = m0 + row;
+        aptr[j] = a.x + size_t(m < a.M ? m : 0) * a.K + swz(row, akc) * 8;
     }
     const uint16_t* bptr[B_CHUNKS];
-    bool bok[B_CHUNKS];
 #pragma unroll
     for (int j = 0; j < B_CHUNKS; ++j) {
-        const int n = n0 + (tid >> 3) + 32 * j;
-        bok[j] = n < a.N;
-        bptr[j] = a.w + size_t(bok[j] ? n : 0) * a.K + akc * 8;
+        const int row = (tid >> 3) + 32 * j;
+        const int n = n0 + row;
+        bptr[j] = a.w + size_t(n < a.N ? n : 0) * a.K + swz(row, akc) * 8;
     }
 
     const int nsteps = a.K / BK;
-    u32x4 areg[2][A_CHUNKS], breg[2][B_CHUNKS];
-    auto gload = [&](int s, auto set) {
-        constexpr int R = decltype(set)::value;
-#pragma unroll
-        for (int j = 0; j < A_CHUNKS; ++j)
-            areg[R][j] = *reinterpret_cast<const u32x4*>(aptr[j] + s * BK);
-#pragma unroll
-        for (int j = 0; j < B_CHUNKS; ++j)
-            breg[R][j] = *reinterpret_cast<const u32x4*>(bptr[j] + s * BK);
-    };
-    auto lstore = [&](int buf, auto set) {
-        constexpr int R = decltype(set)::value;
+    const uint32_t wslot = uint32_t(wave) * 64 * 16;
+    auto tile_load = [&](int s, int buf) {
+        const uint32_t al = lds_addr(&a_lds[buf][0]) + wslot;
+        const uint32_t bl = lds_addr(&b_lds[buf][0]) + wslot;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
         for (int j = 0; j < A_CHUNKS; ++j) {
-            const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&a_lds[buf][row * BK + swz(row, akc) * 8]) = areg[R][j];
+            const uint16_t* p = aptr[j] + s * BK;
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(al + j * 256 * 16);
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(m0) : "memory", "m0");
         }
 #pragma unroll
         for (int j = 0; j < B_CHUNKS; ++j) {
-            const int row = (tid >> 3) + 32 * j;
-            *reinterpret_cast<u32x4*>(&b_lds[buf][row * BK + swz(row, akc) * 8]) = breg[R][j];
+            const uint16_t* p = bptr[j] + s * BK;
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(bl + j * 256 * 16);
+            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(m0) : "memory", "m0");
         }
+#pragma clang diagnostic pop
     };
 
     f32x4 acc[MT][NT];
@@ -151,32 +159,24 @@ __global__ __launch_bounds__(256, 2) void proj_bf16_kernel(ProjArgs a) {
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
         }
     };
-    // step s computes LDS buffer s % 2 from register set s % 2's data; the
-    // loads of step s + 2 go out first, step s + 1's values are stored after
-    auto step = [&](int s, auto set) {
-        constexpr int R = decltype(set)::value;
-        constexpr int Rn = R ^ 1;
-        if (s + 2 < nsteps) gload(s + 2, set);
-        compute(R);
-        if (s + 1 < nsteps) lstore(Rn, std::integral_constant<int, Rn>());
+    // step s: its loads are done, then the barrier (every wave's share is
+    // in LDS and every wave has left step s - 1, whose buffer the loads of
+    // step s + 1 then take), then compute.  Nothing of the compiler's own
+    // is in flight when the first load is issued.
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    tile_load(0, 0);
+    for (int s = 0; s < nsteps; ++s) {
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
-    };
-
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    gload(0, S0());
-    if (nsteps > 1) gload(1, S1());
-    lstore(0, S0());
-    __syncthreads();
-    for (int s = 0; s < nsteps; s += 2) {
-        step(s, S0());
-        if (s + 1 < nsteps) step(s + 1, S1());
+        if (s + 1 < nsteps) tile_load(s + 1, (s + 1) & 1);
+        compute(s & 1);
     }
+    __syncthreads();  // every wave is done with the K-loop buffers
 
     // epilogue, through LDS so that every global store is 16 bytes: acc[i][j][e]
     // (row wm*WM + i*16 + 4*lq + e, column wn*80 + j*16 + l16 of the tile)
-    // plus the bias goes to the tile in LDS as bf16 (the last step ended in a
-    // barrier, so the K-loop buffers are free); then each thread stores rows
+    // plus the bias goes to the tile in LDS as bf16 (after the barrier above
+    // the K-loop buffers are free); then each thread stores rows
     // of 8 columns.  N and the part width are multiples of 64, so 8 columns
     // never straddle a part or the end of N.
 #pragma unroll
