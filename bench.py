@@ -226,9 +226,12 @@ def block_bench(levels, iters):
         xq = x.view(B, Lq, C)
         q, k, v, o = (torch.empty(B, Lq, C, dtype=torch.bfloat16, device="cuda") for _ in range(4))
         y = torch.empty_like(q)
+        # the short ops are timed 10 back-to-back calls per sample (as the
+        # memory-bound ops are), which amortises the event overhead
         qkv_ms, _ = time_op(lambda i: dp.distri_patch_qkv_proj(wl.geom, xq, w["w_qkv"], w["b_qkv"], q, k, v,
-                                                               st["k"], st["v"]), iters)
-        out_ms, _ = time_op(lambda i: dp.distri_patch_out_proj(wl.geom, xq, w["w_o"], w["b_o"], o), iters)
+                                                               st["k"], st["v"]), iters, reps=10)
+        out_ms, _ = time_op(lambda i: dp.distri_patch_out_proj(wl.geom, xq, w["w_o"], w["b_o"], o), iters,
+                            reps=10)
         kw = dict(groups=wl.groups, heads=wl.heads, eps=wl.eps, scale=wl.head_dim ** -0.5)
         ws = torch.empty(dp.distri_patch_block_workspace_size(wl.geom, C, wl.groups, wl.heads,
                                                               dp.DISTRI_BF16), dtype=torch.uint8,
@@ -251,7 +254,8 @@ def block_bench(levels, iters):
                                                                            dp.DISTRI_BF16)),
                           dtype=torch.uint8, device="cuda")
         cx_ms, _ = time_op(lambda i: dp.distri_patch_cross_attn(wl.geom, wl.heads, cx["q"], cx["k_ctx"],
-                                                                cx["v_ctx"], out=co, workspace=cws), iters)
+                                                                cx["v_ctx"], out=co, workspace=cws), iters,
+                            reps=10)
         cx_bytes = 2 * (2 * cx["q"].numel() + 2 * cx["k_ctx"].numel())  # Q, O, context K and V
         cx_fl = 4.0 * B * wl.heads * Lq * 77 * wl.head_dim
         del cx, co, cws
