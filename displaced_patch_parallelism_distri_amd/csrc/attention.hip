@@ -73,15 +73,9 @@ constexpr float kSumLimit = 4096.0f;  // largest lane sum of P kept without movi
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
-#define DP_LDS __attribute__((address_space(3)))
-// s_waitcnt immediates (gfx9 encoding, expcnt and lgkmcnt left free)
-constexpr int kVmcnt0 = 0x0F70;
-constexpr int kVmcntTile = 0x0F70 + 2 * TROWS;  // vmcnt(one tile's loads per thread)
+constexpr int kVmcnt0 = vmcnt_imm(0);
+constexpr int kVmcntTile = vmcnt_imm(2 * TROWS);  // one tile's loads per thread
 
-// byte address in LDS of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return uint32_t(reinterpret_cast<uintptr_t>((const DP_LDS void*)(p)));
-}
 // 16-byte granule swizzles of a K and a V tile row.  K: the 32 rows of an
 // operand read spread over all eight granule positions; V: the eight rows
 // of a transposing read land on both halves of the granule range.
@@ -218,10 +212,8 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
     // that the row's swizzle puts there.  A token row comes from the fresh slice inside the patch,
     // else from the stale map (32-bit offsets: the ABI bounds L * heads * D
     // below 2^31); rows past the map are clamped to its last row, whose keys
-    // the last tile masks.  The loads are written in asm: the compiler would
-    // otherwise wait for every load into LDS before any LDS read, which
-    // serialises the pipeline; their completion is the explicit vmcnt wait
-    // at the top of each tile instead.  They have no register results.
+    // the last tile masks.  Their completion is the explicit vmcnt wait at
+    // the top of each tile (global_load_lds16).
     const int c8 = tid & 7;
     const uint16_t* kst = a.ks + (b * a.L * a.heads + hd) * D;
     const uint16_t* vst = a.vs + (b * a.L * a.heads + hd) * D;
@@ -239,15 +231,8 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
             const uint16_t* kp = (fresh ? kfr : kst) + off + (c8 ^ k_swizzle(krow)) * 8;
             const uint16_t* vp = (fresh ? vfr : vst) + off + (c8 ^ v_swizzle(krow)) * 8;
             const uint32_t slot = uint32_t(j * NWAVES * 64 + wave * 64) * 16;
-            const uint32_t m0k = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][0][0]) + slot);
-            const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr(&kv_lds[stage][1][0]) + slot);
-            // (m0 is written inside each asm statement; this kernel keeps
-            // nothing else in m0, a register the compiler reserves)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(kp), "s"(m0k) : "memory", "m0");
-            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(vp), "s"(m0v) : "memory", "m0");
-#pragma clang diagnostic pop
+            global_load_lds16(kp, lds_addr(&kv_lds[stage][0][0]) + slot);
+            global_load_lds16(vp, lds_addr(&kv_lds[stage][1][0]) + slot);
         }
     };
     // K operand (row kb*32 + lr, dims ks*16 + g*8 ..): granule 2 ks + g of

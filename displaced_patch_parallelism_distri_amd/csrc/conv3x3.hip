@@ -61,13 +61,7 @@ struct ConvArgs {
     int mtiles, ntiles;
 };
 
-#define DP_LDS __attribute__((address_space(3)))
-// byte address in LDS of a __shared__ object
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return uint32_t(reinterpret_cast<uintptr_t>((const DP_LDS void*)(p)));
-}
-// s_waitcnt immediate for vmcnt(0) (gfx9 encoding, expcnt and lgkmcnt free)
-constexpr int kVmcnt0 = 0x0F70;
+constexpr int kVmcnt0 = vmcnt_imm(0);
 
 // 16-byte chunk position of chunk `c` of LDS row `r`
 __device__ __forceinline__ int swz(int r, int c) { return c ^ ((r >> 1) & 7); }
@@ -146,11 +140,8 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
     // granules j*256 + w*64 + lane, i.e. row (tid >> 3) + 32 j at physical
     // chunk tid & 7, so the thread reads the logical chunk stored there.
     // Padding rows read zeros and weight rows past Cout read row 0 (they
-    // feed only output columns that are never stored).  The loads are
-    // inline asm with no register results: the compiler would otherwise
-    // wait for every load into LDS before any LDS read; their completion is
-    // the explicit wait at the top of each step.  m0 is written inside each
-    // asm statement; this kernel keeps nothing else in m0.
+    // feed only output columns that are never stored).  Their completion is
+    // the explicit wait at the top of each step (global_load_lds16).
     int alc[A_CHUNKS], blc[B_CHUNKS];
 #pragma unroll
     for (int j = 0; j < A_CHUNKS; ++j) alc[j] = swz((tid >> 3) + 32 * j, akc) * 8;
@@ -163,21 +154,11 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
         if (ci0 == 0) set_tap(tap);
         const uint32_t al = lds_addr(&a_lds[buf][0]) + wslot;
         const uint32_t bl = lds_addr(&b_lds[buf][0]) + wslot;
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
 #pragma unroll
-        for (int j = 0; j < A_CHUNKS; ++j) {
-            const uint16_t* p = aptr[j] + ci0 + alc[j];
-            const uint32_t m0 = __builtin_amdgcn_readfirstlane(al + j * 256 * 16);
-            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(m0) : "memory", "m0");
-        }
+        for (int j = 0; j < A_CHUNKS; ++j) global_load_lds16(aptr[j] + ci0 + alc[j], al + j * 256 * 16);
 #pragma unroll
-        for (int j = 0; j < B_CHUNKS; ++j) {
-            const uint16_t* p = bptr[j] + tap * a.cin + ci0 + blc[j];
-            const uint32_t m0 = __builtin_amdgcn_readfirstlane(bl + j * 256 * 16);
-            asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(p), "s"(m0) : "memory", "m0");
-        }
-#pragma clang diagnostic pop
+        for (int j = 0; j < B_CHUNKS; ++j)
+            global_load_lds16(bptr[j] + tap * a.cin + ci0 + blc[j], bl + j * 256 * 16);
     };
 
     f32x4 acc[MT][NT];

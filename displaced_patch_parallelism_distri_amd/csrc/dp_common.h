@@ -73,6 +73,37 @@ struct F32T {
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS tile loads (gfx950 global_load_lds_dwordx4).
+#define DP_LDS __attribute__((address_space(3)))
+
+// byte address in LDS of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const DP_LDS void*)(p)));
+}
+
+// One 16-byte load per lane straight into LDS: lane l's 16 bytes at `src`
+// land at LDS byte address lds_base + 16 l (lds_base is wave-uniform).  No
+// register receives the data and no LDS store instruction is issued.
+// Written in asm: with the compiler's builtin for this load, the compiler
+// waits for every outstanding load into LDS before any LDS read, which
+// serialises a multi-stage pipeline; callers wait with s_waitcnt vmcnt
+// (vmcnt_wait below) before the barrier that precedes a stage's use, and
+// keep nothing of their own in flight across it.  m0 is written inside the
+// asm statement; no kernel of this library keeps anything else in m0 (a
+// register the compiler reserves, hence the silenced warning).
+__device__ __forceinline__ void global_load_lds16(const void* src, uint32_t lds_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
+#pragma clang diagnostic pop
+}
+
+// s_waitcnt immediate for vmcnt(n), n < 16 (gfx9 encoding: expcnt and
+// lgkmcnt left free)
+constexpr int vmcnt_imm(int n) { return 0x0F70 + n; }
+
+// ---------------------------------------------------------------------------
 // Internal launchers.  Arguments are already validated by the ABI layer.
 struct Geom {
     int64_t B, H, W, n, i;
