@@ -87,16 +87,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // Written in asm: with the compiler's builtin for this load, the compiler
 // waits for every outstanding load into LDS before any LDS read, which
 // serialises a multi-stage pipeline; callers wait with s_waitcnt vmcnt
-// (vmcnt_wait below) before the barrier that precedes a stage's use, and
-// keep nothing of their own in flight across it.  m0 is written inside the
-// asm statement; no kernel of this library keeps anything else in m0 (a
-// register the compiler reserves, hence the silenced warning).
+// (vmcnt_imm below) before the barrier that precedes a stage's use, and
+// keep nothing of their own in flight across it.  The load takes its LDS
+// address from m0, a register the compiler reserves: the asm saves m0,
+// sets it and restores it, so whatever the compiler keeps there survives.
 __device__ __forceinline__ void global_load_lds16(const void* src, uint32_t lds_base) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base);
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0) : "memory", "m0");
-#pragma clang diagnostic pop
+    uint32_t saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %1, off\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(src), "s"(m0)
+        : "memory");
 }
 
 // s_waitcnt immediate for vmcnt(n), n < 16 (gfx9 encoding: expcnt and
