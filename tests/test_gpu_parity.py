@@ -30,9 +30,14 @@ def _gpu():
 W = si.WORKLOADS
 RAGGED_BF16 = si.Workload("ragged_bf16", 1, 128, 20, 13, 4, 2, seed=2024)     # Lq=65, L=260
 RAGGED_F32 = si.Workload("ragged_f32", 2, 64, 12, 7, 3, 1, dtype="f32", sigma=0.05, seed=2025)
+# one partial key tile (L = 32) and 16 queries: a single task, seven idle waves
+TINY_L_BF16 = si.Workload("tiny_l_bf16", 1, 128, 4, 8, 2, 2, seed=2026)          # Lq=16, L=32
+# one full 512-query tile plus a partial one (88 queries), 3 heads, L = 600
+TAIL_BF16 = si.Workload("tail_bf16", 1, 192, 30, 20, 1, 3, seed=2027)            # Lq=L=600
 FULL_CASES = [(W["tiny"], 0), (W["tiny"], 1), (W["sdxl1024_l2"], 0), (W["sdxl1024_l2"], 3),
               (W["sdxl1024_l2"], 7), (W["sdxl1024_l3"], 1), (W["sdxl1024_l3"], 3),
-              (RAGGED_BF16, 0), (RAGGED_BF16, 2), (RAGGED_BF16, 3), (RAGGED_F32, 1)]
+              (RAGGED_BF16, 0), (RAGGED_BF16, 2), (RAGGED_BF16, 3), (RAGGED_F32, 1),
+              (TINY_L_BF16, 1), (TAIL_BF16, 0)]
 SAMPLED_CASES = [(W["sdxl2048_l2"], 4), (W["sdxl3840_l2"], 0), (W["sdxl3840_l2"], 4),
                  (W["sdxl3840_l2"], 7), (W["sdxl3840_l3"], 4)]
 
