@@ -50,14 +50,15 @@ def test_cross_attention(wl, patch, ctx):
         assert np.array_equal(to_np(out), np.broadcast_to(v, ref.shape))
 
 
-def test_cross_attention_full_size_sampled():
-    wl = W["sdxl3840_l2"].with_patch(4)
+@pytest.mark.parametrize("name", ["sdxl3840_l2", "sdxl3840_l3"])
+def test_cross_attention_full_size_sampled(name):
+    wl = W[name].with_patch(4)
     d = si.make_cross_inputs(wl, 77)
     g = {k: v.cuda() for k, v in d.items()}
     out = to_np(dp.distri_patch_cross_attn(wl.geom, wl.heads, g["q"], g["k_ctx"], g["v_ctx"]))
     for r0, r1 in sample_rows(wl.lq, 256, 4):
         ref = oracle.cross_attn(0.125, d["q"][:, r0:r1], d["k_ctx"], d["v_ctx"])
-        assert_close(out[:, r0:r1], ref, wl.dtype, f"cross-attention 3840 rows {r0}:{r1}")
+        assert_close(out[:, r0:r1], ref, wl.dtype, f"cross-attention {name} rows {r0}:{r1}")
 
 
 NAIVE_CASES = [(W["tiny"], 1), (W["sdxl1024_l2"], 3), (RAGGED, 0)]
