@@ -168,6 +168,20 @@ def _stream(stream):
     return ctypes.c_void_p(int(stream))
 
 
+def _record(stream, *tensors):
+    """Tensors allocated here (on torch's current stream) but used by a launch
+    on another ``stream``: tell the caching allocator, so that it does not
+    hand their memory to other work before that stream is done with them."""
+    if stream is None:
+        return
+    ts = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream))
+    if ts.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if t is not None and t.numel() > 0:
+            t.record_stream(ts)
+
+
 def distri_patch_self_attn_workspace_size(g, heads, head_dim, dtype_code) -> int:
     n = ctypes.c_size_t(0)
     _check(load().distri_patch_self_attn_workspace_size(ctypes.byref(_as_geom(g)), heads,
@@ -184,14 +198,22 @@ def distri_async_groupnorm_workspace_size(g, channels, groups, dtype_code) -> in
     return int(n.value)
 
 
-def _workspace(nbytes, ref, workspace):
+def _workspace(nbytes, ref, workspace, stream=None):
     if nbytes == 0:
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=ref.device)
+        _record(stream, workspace)
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
     return workspace, workspace.numel() * workspace.element_size()
+
+
+def _new(stream, shape, like, dtype=None):
+    """An output tensor allocated here for a launch on ``stream``."""
+    t = torch.empty(shape, dtype=like.dtype if dtype is None else dtype, device=like.device)
+    _record(stream, t)
+    return t
 
 
 def distri_patch_self_attn(g, heads, q, k_fresh, v_fresh, k_stale, v_stale, out=None,
@@ -201,14 +223,14 @@ def distri_patch_self_attn(g, heads, q, k_fresh, v_fresh, k_stale, v_stale, out=
     g = _as_geom(g)
     code = _dtype_code(q)
     if out is None:
-        out = torch.empty_like(q)
+        out = _new(stream, q.shape, q)
     if scale is None:
         scale = head_dim ** -0.5
     lq = (g.height // max(g.n_patches, 1)) * g.width
     nl = g.batch * lq * heads * head_dim
     nf = g.batch * g.height * g.width * heads * head_dim
     ws_bytes = distri_patch_self_attn_workspace_size(g, heads, head_dim, code)
-    ws, ws_len = _workspace(ws_bytes, q, workspace)
+    ws, ws_len = _workspace(ws_bytes, q, workspace, stream)
     st = load().distri_patch_self_attn(
         ctypes.byref(g), heads, head_dim, float(scale), code,
         _ptr(q, "q", q.dtype, nl), _ptr(k_fresh, "k_fresh", q.dtype, nl),
@@ -227,7 +249,7 @@ def distri_patch_conv3x3_halo(g, x_fresh, x_stale, weight, bias=None, y=None, st
     cout, cin = weight.shape[0], weight.shape[-1]
     h = g.height // max(g.n_patches, 1)
     if y is None:
-        y = torch.empty((g.batch, h, g.width, cout), dtype=x_fresh.dtype, device=x_fresh.device)
+        y = _new(stream, (g.batch, h, g.width, cout), x_fresh)
     st = load().distri_patch_conv3x3_halo(
         ctypes.byref(g), cin, cout, code,
         _ptr(x_fresh, "x_fresh", x_fresh.dtype, g.batch * h * g.width * cin),
@@ -260,7 +282,7 @@ def distri_group_moments(g, groups, x_fresh, table, workspace=None, stream=None)
     code = _dtype_code(x_fresh)
     C = x_fresh.shape[-1]
     ws_bytes = distri_async_groupnorm_workspace_size(g, C, groups, code)
-    ws, ws_len = _workspace(ws_bytes, x_fresh, workspace)
+    ws, ws_len = _workspace(ws_bytes, x_fresh, workspace, stream)
     st = load().distri_group_moments(
         ctypes.byref(g), C, groups, code, _ptr(x_fresh, "x_fresh", x_fresh.dtype),
         _ptr(table, "table", torch.float32, g.batch * g.n_patches * groups * 2),
@@ -275,11 +297,11 @@ def _groupnorm(func, g, groups, x_fresh, stale_moments, gamma, beta, eps, y, fre
     code = _dtype_code(x_fresh)
     C = x_fresh.shape[-1]
     if y is None:
-        y = torch.empty_like(x_fresh)
+        y = _new(stream, x_fresh.shape, x_fresh)
     if fresh_moments is None:
-        fresh_moments = torch.empty((g.batch, groups, 2), dtype=torch.float32, device=x_fresh.device)
+        fresh_moments = _new(stream, (g.batch, groups, 2), x_fresh, torch.float32)
     ws_bytes = distri_async_groupnorm_workspace_size(g, C, groups, code)
-    ws, ws_len = _workspace(ws_bytes, x_fresh, workspace)
+    ws, ws_len = _workspace(ws_bytes, x_fresh, workspace, stream)
     st = getattr(load(), func)(
         ctypes.byref(g), C, groups, float(eps), code, _ptr(x_fresh, "x_fresh", x_fresh.dtype),
         _ptr(stale_moments, "stale_moments", torch.float32, g.batch * g.n_patches * groups * 2),
@@ -314,9 +336,9 @@ def distri_patch_qkv_proj(g, x, w_qkv, bias=None, q=None, k_fresh=None, v_fresh=
     C = x.shape[-1]
     lq = (g.height // max(g.n_patches, 1)) * g.width
     shape = (g.batch, lq, C)
-    q = torch.empty(shape, dtype=x.dtype, device=x.device) if q is None else q
-    k_fresh = torch.empty(shape, dtype=x.dtype, device=x.device) if k_fresh is None else k_fresh
-    v_fresh = torch.empty(shape, dtype=x.dtype, device=x.device) if v_fresh is None else v_fresh
+    q = _new(stream, shape, x) if q is None else q
+    k_fresh = _new(stream, shape, x) if k_fresh is None else k_fresh
+    v_fresh = _new(stream, shape, x) if v_fresh is None else v_fresh
     n_tok = g.batch * lq * C
     n_full = g.batch * g.height * g.width * C
     st = load().distri_patch_qkv_proj(
@@ -337,7 +359,7 @@ def distri_patch_out_proj(g, o, w_o, bias=None, y=None, stream=None):
     C = w_o.shape[0]
     lq = (g.height // max(g.n_patches, 1)) * g.width
     if y is None:
-        y = torch.empty((g.batch, lq, C), dtype=o.dtype, device=o.device)
+        y = _new(stream, (g.batch, lq, C), o)
     n_tok = g.batch * lq * C
     st = load().distri_patch_out_proj(
         ctypes.byref(g), C, code, _ptr(o, "o", o.dtype, n_tok), _ptr(w_o, "w_o", o.dtype, C * C),
@@ -402,13 +424,12 @@ def distri_patch_block(g, weights, x, state_in, state_out=None, y=None, groups=3
     C = x.shape[-1]
     heads = C // 64 if heads is None else heads
     if y is None:
-        y = torch.empty((g.batch, (g.height // max(g.n_patches, 1)) * g.width, C), dtype=x.dtype,
-                        device=x.device)
+        y = _new(stream, (g.batch, (g.height // max(g.n_patches, 1)) * g.width, C), x)
     bw = _block_weights(weights, C, groups, heads, eps, scale, x.dtype)
     sin = _block_state(state_in, g, C, groups, x.dtype)
     sout = sin if state_out is None else _block_state(state_out, g, C, groups, x.dtype)
     ws_bytes = distri_patch_block_workspace_size(g, C, groups, heads, code)
-    ws, ws_len = _workspace(ws_bytes, x, workspace)
+    ws, ws_len = _workspace(ws_bytes, x, workspace, stream)
     st = load().distri_patch_block(
         ctypes.byref(g), ctypes.byref(bw), code, _ptr(x, "x", x.dtype, y.numel()),
         _ptr(y, "y", x.dtype, y.numel()), ctypes.byref(sin), ctypes.byref(sout),
@@ -428,11 +449,11 @@ def distri_patch_block_sync(g, weights, x, state, y=None, groups=32, heads=None,
     n = g.n_patches
     lq = (g.height // max(n, 1)) * g.width
     if y is None:
-        y = torch.empty((n, g.batch, lq, C), dtype=x.dtype, device=x.device)
+        y = _new(stream, (n, g.batch, lq, C), x)
     bw = _block_weights(weights, C, groups, heads, eps, scale, x.dtype)
     bs = _block_state(state, g, C, groups, x.dtype)
     ws_bytes = distri_patch_block_sync_workspace_size(g, C, groups, heads, code)
-    ws, ws_len = _workspace(ws_bytes, x, workspace)
+    ws, ws_len = _workspace(ws_bytes, x, workspace, stream)
     st = load().distri_patch_block_sync(
         ctypes.byref(g), ctypes.byref(bw), code, _ptr(x, "x", x.dtype, y.numel()),
         _ptr(y, "y", x.dtype, y.numel()), ctypes.byref(bs), _ptr(ws, "workspace"), ws_len,
@@ -457,14 +478,14 @@ def distri_patch_cross_attn(g, heads, q, k_ctx, v_ctx, out=None, scale=None, hea
     code = _dtype_code(q)
     ctx_len = k_ctx.shape[1]
     if out is None:
-        out = torch.empty_like(q)
+        out = _new(stream, q.shape, q)
     if scale is None:
         scale = head_dim ** -0.5
     lq = (g.height // max(g.n_patches, 1)) * g.width
     nl = g.batch * lq * heads * head_dim
     nc = g.batch * ctx_len * heads * head_dim
     ws_bytes = distri_patch_cross_attn_workspace_size(g, heads, ctx_len, code, head_dim)
-    ws, ws_len = _workspace(ws_bytes, q, workspace)
+    ws, ws_len = _workspace(ws_bytes, q, workspace, stream)
     st = load().distri_patch_cross_attn(
         ctypes.byref(g), heads, head_dim, ctx_len, float(scale), code, _ptr(q, "q", q.dtype, nl),
         _ptr(k_ctx, "k_ctx", q.dtype, nc), _ptr(v_ctx, "v_ctx", q.dtype, nc),

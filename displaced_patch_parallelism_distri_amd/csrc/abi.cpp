@@ -124,7 +124,11 @@ int distri_patch_self_attn(const distri_patch_geom* g, int64_t heads, int64_t he
         DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
                  "attention workspace missing or too small");
         DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
-        DP_CHECK(!overlaps({workspace, need}, o), DISTRI_ERR_ALIAS, "workspace overlaps out");
+        const Range w{workspace, need};
+        DP_CHECK(!overlaps(w, o) && !overlaps(w, {q, local}) && !overlaps(w, {k_fresh, local}) &&
+                     !overlaps(w, {v_fresh, local}) && !overlaps(w, {k_stale, full}) &&
+                     !overlaps(w, {v_stale, full}),
+                 DISTRI_ERR_ALIAS, "workspace overlaps an input or out");
     }
     return hip_status(dp::launch_attention(gg, heads, scale, dtype == DISTRI_BF16, q, k_fresh,
                                            v_fresh, k_stale, v_stale, out, workspace,
@@ -171,7 +175,10 @@ int distri_patch_cross_attn(const distri_patch_geom* g, int64_t heads, int64_t h
         DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
                  "attention workspace missing or too small");
         DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
-        DP_CHECK(!overlaps({workspace, need}, o), DISTRI_ERR_ALIAS, "workspace overlaps out");
+        const Range w{workspace, need};
+        DP_CHECK(!overlaps(w, o) && !overlaps(w, {q, local}) && !overlaps(w, {k_ctx, ctx}) &&
+                     !overlaps(w, {v_ctx, ctx}),
+                 DISTRI_ERR_ALIAS, "workspace overlaps an input or out");
     }
     if (short_ctx)  // the whole context held in LDS
         return hip_status(dp::launch_cross_attention(gg.B, gg.lq(), ctx_len, heads, scale, q, k_ctx,

@@ -25,12 +25,19 @@
 //    XCD's L2;
 //  * key tiles of 64 rows go from global memory straight into LDS
 //    (global_load_lds_dwordx4: no registers, no LDS store instructions) in
-//    three stages, the loads two tiles ahead of their use.  K and V are
+//    four stages, the loads three tiles ahead of their use.  K and V are
 //    both kept row-major, each row's 16-byte granules XOR-swizzled so that
 //    the operand reads hit every LDS bank evenly: K rows are the MFMA A
 //    operand of S^T = K Q^T (ds_read_b128), and the V^T operand of O^T =
 //    V^T P^T comes from the transposing read ds_read_b64_tr_b16 (a 16-lane
 //    group turns 16 4-element row pieces into 4-key columns);
+//  * the PV product runs in f16 (v_mfma_f32_32x32x16_f16): P rounded to f16
+//    carries 11 significant bits against bf16's 8, which keeps the error of
+//    the weights well below the output's own bf16 rounding.  Each V tile is
+//    rewritten in LDS from bf16 to f16 once per block, a tile ahead of its
+//    use (8 elements per thread), so the waves read f16 operands directly.
+//    The bf16 -> f16 map is exact for |v| in [2^-14, 65504]; V elements of
+//    magnitude 65536 or more become inf (a documented input range);
 //  * S is computed transposed (keys x queries) with v_mfma_f32_32x32x16_bf16:
 //    a lane then holds 16 keys of ONE query per 32x32 block, so the row max and
 //    row sum are in-lane reductions plus one exchange between the two
@@ -41,12 +48,12 @@
 //    leaves [0, kSumLimit] (the first tile, where m = -inf, or a score above
 //    m by about log2(kSumLimit)) does the wave take a rare, wave-uniform
 //    branch that forms S again, takes the row max, rescales O and l and
-//    recomputes P.  P then stays at most kSumLimit, which bf16 and the fp32
+//    recomputes P.  P then stays at most kSumLimit, which f16 and the fp32
 //    accumulators carry with the same relative precision.  The row sum l
-//    adds the bf16-rounded P (v_dot2_f32_bf16) so numerator and denominator
+//    adds the f16-rounded P (v_dot2_f32_f16) so numerator and denominator
 //    carry the same rounding - a row dominated by one key then returns that
 //    key's V exactly;
-//  * P is rounded to bf16 and fed straight from the S^T accumulators into the
+//  * P is rounded to f16 and fed straight from the S^T accumulators into the
 //    PV MFMA as its B operand (the accumulator layout already matches the
 //    operand layout, with the V^T reads permuted to agree).
 // fp32 kernel: one thread per query, K/V tiles in LDS, fp32 online softmax
@@ -67,7 +74,7 @@ constexpr int BLOCKS_PER_CU = 8 / NWAVES;  // two waves per SIMD either way
 constexpr int TROWS = KT * 8 / (NWAVES * 64);  // K (and V) tile rows one thread loads
 constexpr int QB = 2;        // 32-query blocks per wave
 constexpr int QTILE = NWAVES * QB * 32;
-constexpr int NSTAGE = 3;       // K/V tile stages in LDS (loads run two tiles ahead)
+constexpr int NSTAGE = 4;       // K/V tile stages in LDS (loads run three tiles ahead)
 constexpr int kPartialCost = 3; // cost of one partial write + merge, in key tiles
 constexpr float kSumLimit = 4096.0f;  // largest lane sum of P kept without moving the max
 
@@ -126,7 +133,12 @@ struct AttnArgs {
     Plan plan;
 };
 
-Plan make_plan(int64_t B, int64_t heads, int64_t lq, int64_t L, int cus) {
+// The work plan is made for a fixed machine of kPlanCUs compute units (an
+// MI355X), so that the workspace it needs is a function of the call's sizes
+// alone; on a device with fewer CUs the same grid runs in more rounds.
+constexpr int kPlanCUs = 256;
+
+Plan make_plan(int64_t B, int64_t heads, int64_t lq, int64_t L, int cus = kPlanCUs) {
     Plan p;
     p.nqt = int(ceil_div(lq, QTILE));
     p.nfull = int(lq / QTILE);
@@ -162,9 +174,10 @@ __device__ __forceinline__ int xcd_remap(int w, int n) {
 
 __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(AttnArgs a) {
     // NSTAGE stages of [K tile | V tile], each 64 rows x 128 bytes, row t's
-    // 16-byte granule c stored at position c ^ swizzle(t)
+    // 16-byte granule c stored at position c ^ swizzle(t).  K stays bf16; a
+    // V tile arrives as bf16 and is rewritten in place as f16 before its PV.
     __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NSTAGE][2][KT * D];
-    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+    const f16x2 kOnes = {(_Float16)1.0f, (_Float16)1.0f};
     const Plan& pl = a.plan;
 
     // ---- which (task, key range) this block owns
@@ -235,6 +248,20 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
             global_load_lds16(vp, lds_addr(&kv_lds[stage][1][0]) + slot);
         }
     };
+    // V tile of a stage, bf16 -> f16 in place: each thread rewrites 16-byte
+    // pieces of it (which piece does not matter: the map is element-wise).
+    // The PV product then multiplies f16 P by f16 V.
+    auto convert_v = [&](int stage) {
+#pragma unroll
+        for (int j = 0; j < TROWS; ++j) {
+            u32x4* vp = reinterpret_cast<u32x4*>(&kv_lds[stage][1][0]) + tid + j * NWAVES * 64;
+            const u32x4 w = *vp;
+            u32x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h[e] = bf16x2_to_f16x2(w[e]);
+            *vp = h;
+        }
+    };
     // K operand (row kb*32 + lr, dims ks*16 + g*8 ..): granule 2 ks + g of
     // the row, swizzled; the row's swizzle depends on lr only
     const int ksw = k_swizzle(lr);
@@ -300,10 +327,10 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
                 }
         }
     };
-    // P = exp2(s * c - m[qb]) rounded to bf16, and the lane's sum of those
-    // rounded values (the row sum adds the bf16-rounded p that the PV MFMA
+    // P = exp2(s * c - m[qb]) rounded to f16, and the lane's sum of those
+    // rounded values (the row sum adds the f16-rounded p that the PV MFMA
     // multiplies, so the normalisation matches the numerator)
-    auto softmax = [&](const f32x16 (&s)[2][QB], int qb, bf16x8 (&p)[2][2]) {
+    auto softmax = [&](const f32x16 (&s)[2][QB], int qb, f16x8 (&p)[2][2]) {
         const float mneg = -m[qb];
         float rsum = 0.f;
 #pragma unroll
@@ -313,17 +340,17 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
                 uint32_t w[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    w[e] = pack_bf16x2(
+                    w[e] = pack_f16x2(
                         __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e], a.c, mneg)),
                         __builtin_amdgcn_exp2f(fmaf(s[kb][qb][h2 * 8 + 2 * e + 1], a.c, mneg)));
                 // (scalar words on purpose: passing vector elements w[e]
                 // straight to the builtin made hipcc read w[0] four times)
                 const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rsum, false);
-                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rsum, false);
-                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rsum, false);
-                rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rsum, false);
-                p[kb][h2] = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+                rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), kOnes, rsum, false);
+                rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), kOnes, rsum, false);
+                rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w2), kOnes, rsum, false);
+                rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w3), kOnes, rsum, false);
+                p[kb][h2] = __builtin_bit_cast(f16x8, u32x4{w0, w1, w2, w3});
             }
         }
         return rsum;
@@ -339,16 +366,19 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
     // leaves its SIMD to the wave of the block that shares it.
     auto tile = [&](int kt, auto kMask) {
         const int cur = (kt - kt0) % NSTAGE;
-        // this thread's loads of tile kt are done (those of tile kt + 1,
-        // 2 TROWS per thread, may still be in flight); after the barrier every
-        // wave's share is in LDS and every wave has left tile kt - 1, whose
-        // stage the loads of tile kt + 2 then take
-        if (kt + 1 < kt1)
+        // this thread's loads of tiles kt and kt + 1 are done (those of tile
+        // kt + 2, 2 TROWS per thread, may still be in flight); after the
+        // barrier every wave's share of both is in LDS, V of tile kt is f16
+        // (converted during tile kt - 1), and every wave has left tile
+        // kt - 1, whose stage the loads of tile kt + 3 then take.  V of tile
+        // kt + 1 is converted now, for the next tile.
+        if (kt + 2 < kt1)
             __builtin_amdgcn_s_waitcnt(kVmcntTile);
         else
             __builtin_amdgcn_s_waitcnt(kVmcnt0);
         __syncthreads();
-        if (kt + 2 < kt1) tile_load(kt + 2, (kt + 2 - kt0) % NSTAGE);
+        if (kt + 3 < kt1) tile_load(kt + 3, (kt + 3 - kt0) % NSTAGE);
+        if (kt + 1 < kt1) convert_v((kt + 1 - kt0) % NSTAGE);
         if (wave_active) {
             f32x16 s[2][QB];
             // one query block after the other, so that the second block's
@@ -358,7 +388,7 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
 #pragma unroll
             for (int qb = 0; qb < QB; ++qb) {
                 // fast path: P against the current reference max, no row max
-                bf16x8 p[2][2];
+                f16x8 p[2][2];
                 float rsum = softmax(s, qb, p);
                 // the reference max moves only when some lane's sum of P
                 // leaves [0, kSumLimit] (always on the first tile, where m =
@@ -403,10 +433,10 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
                             const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DP_LDS i16x4*)(vb));
                             const i16x4 hi =
                                 __builtin_amdgcn_ds_read_tr16_b64_v4i16((DP_LDS i16x4*)(vb + 8 * 128));
-                            const bf16x8 va = __builtin_bit_cast(
-                                bf16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
-                            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kb][h2], o[db][qb],
-                                                                                0, 0, 0);
+                            const f16x8 va = __builtin_bit_cast(
+                                f16x8, i16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+                            o[db][qb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, p[kb][h2], o[db][qb],
+                                                                               0, 0, 0);
                         }
                     }
                 }
@@ -420,6 +450,16 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     tile_load(kt0, 0);
     if (kt0 + 1 < kt1) tile_load(kt0 + 1, 1);
+    if (kt0 + 2 < kt1) tile_load(kt0 + 2, 2);
+    // the first tile's V is converted here; every later one a tile ahead
+    if (kt0 + 2 < kt1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(4 * TROWS));
+    else if (kt0 + 1 < kt1)
+        __builtin_amdgcn_s_waitcnt(kVmcntTile);
+    else
+        __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    convert_v(0);
     const int full_end = (kt1 == pl.nkt && a.L % KT != 0) ? kt1 - 1 : kt1;
     for (int kt = kt0; kt < full_end; ++kt) tile(kt, std::false_type{});
     if (full_end < kt1) tile(full_end, std::true_type{});
@@ -583,9 +623,7 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(AttnArgsF32 a) {
 
 size_t attention_workspace_bytes(int64_t B, int64_t lq, int64_t L, int64_t heads, bool bf16) {
     if (!bf16) return 0;
-    const int cus = device_cus();
-    if (cus <= 0) return 0;
-    const Plan p = make_plan(B, heads, lq, L, cus);
+    const Plan p = make_plan(B, heads, lq, L);
     return size_t(p.partials()) * QTILE * (D + 2) * sizeof(float);
 }
 
@@ -605,8 +643,6 @@ hipError_t launch_attention_rows(int64_t B, int64_t lq, int64_t L, int64_t own_l
                                  const void* vf, const void* ks, const void* vs, void* out,
                                  void* ws, hipStream_t s) {
     if (bf16) {
-        const int cus = device_cus();
-        if (cus <= 0) return hipErrorNoDevice;
         AttnArgs a;
         a.q = static_cast<const uint16_t*>(q);
         a.kf = static_cast<const uint16_t*>(kf);
@@ -614,7 +650,7 @@ hipError_t launch_attention_rows(int64_t B, int64_t lq, int64_t L, int64_t own_l
         a.ks = static_cast<const uint16_t*>(ks);
         a.vs = static_cast<const uint16_t*>(vs);
         a.out = static_cast<uint16_t*>(out);
-        a.plan = make_plan(B, heads, lq, L, cus);
+        a.plan = make_plan(B, heads, lq, L);
         a.part_o = static_cast<float*>(ws);
         a.part_ml = a.part_o + a.plan.partials() * D * QTILE;
         a.lq = int(lq);

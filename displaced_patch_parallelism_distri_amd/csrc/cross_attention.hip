@@ -10,14 +10,17 @@
 // chunks) is not needed: a block stages the whole context of its (image,
 // head) once and its 4 waves then stream 32-query blocks through it, each
 // block in one pass with the exact row max:
-//  * K row-major and V transposed (V^T[d][key]) in LDS, keys past ctx zero;
+//  * K row-major (bf16) and V transposed (V^T[d][key]) in LDS as f16, keys
+//    past ctx zero;
 //  * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (a lane holds 16 keys of one
 //    query per 32-key block, as in the self-attention kernel), keys past ctx
 //    set to -inf, the row max over all keys in registers plus one exchange
 //    between the half-waves;
-//  * P = exp2(s c - max c) rounded to bf16 straight into the PV MFMA's B
-//    operand, the row sum over the same rounded values; 16-key groups that
-//    lie wholly past ctx are skipped;
+//  * P = exp2(s c - max c) rounded to f16 straight into the PV MFMA's B
+//    operand (v_mfma_f32_32x32x16_f16: 11 significant bits for the weights,
+//    against bf16's 8), the row sum over the same rounded values; 16-key
+//    groups that lie wholly past ctx are skipped.  V elements of magnitude
+//    65536 or more become inf in f16 (a documented input range);
 //  * the next query block's Q is loaded while the current one computes, and
 //    O leaves through 16-byte stores after one lane exchange.
 // The grid runs all heads of one token range next to each other, so blocks
@@ -57,7 +60,7 @@ __global__ __launch_bounds__(256, 3) void attn_ctx_bf16_kernel(CtxArgs a) {
     constexpr int VPITCH = NK + 4;    // V^T row pitch: 2 x odd dwords, no bank conflicts
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[NK * KPITCH];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[D * VPITCH];
-    const bf16x2 kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+    const f16x2 kOnes = {(_Float16)1.0f, (_Float16)1.0f};
 
     const int bh = int(blockIdx.x % unsigned(a.bh));
     const int chunk = int(blockIdx.x / unsigned(a.bh));
@@ -110,10 +113,12 @@ __global__ __launch_bounds__(256, 3) void attn_ctx_bf16_kernel(CtxArgs a) {
                                        : u32x4{0, 0, 0, 0};
             const u32x4 v1 = t + 1 < a.ctx ? *reinterpret_cast<const u32x4*>(vb + (t + 1) * rs + c8 * 8)
                                            : u32x4{0, 0, 0, 0};
+            // dims 2j and 2j + 1 of keys (t, t + 1), each pair as f16
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t lo = __builtin_amdgcn_perm(v1[j], v0[j], 0x05040100u);
-                const uint32_t hi = __builtin_amdgcn_perm(v1[j], v0[j], 0x07060302u);
+                const uint32_t lo = pack_f16x2(__uint_as_float(v0[j] << 16), __uint_as_float(v1[j] << 16));
+                const uint32_t hi = pack_f16x2(__uint_as_float(v0[j] & 0xffff0000u),
+                                               __uint_as_float(v1[j] & 0xffff0000u));
                 *reinterpret_cast<uint32_t*>(&v_lds[(c8 * 8 + 2 * j) * VPITCH + t]) = lo;
                 *reinterpret_cast<uint32_t*>(&v_lds[(c8 * 8 + 2 * j + 1) * VPITCH + t]) = hi;
             }
@@ -160,25 +165,25 @@ __global__ __launch_bounds__(256, 3) void attn_ctx_bf16_kernel(CtxArgs a) {
                                                          false);
         const float mneg = -__builtin_fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * a.c;
 
-        // P in bf16 and its row sum; O^T = V^T P^T.  B operand slot e of the
+        // P in f16 and its row sum; O^T = V^T P^T.  B operand slot e of the
         // k-step (kb, h2) holds key kb*32 + h2*16 + (e/4)*8 + 4g + e%4 (the
         // S^T accumulator layout); the V^T operand reads those same keys.
         f32x16 o[2] = {f32x16{}, f32x16{}};
         float rsum = 0.f;
         // V^T operands of 16-key group gi = 2 kb + h2 for both 32-dim halves
-        auto vread = [&](int gi, bf16x8 (&va)[2]) {
+        auto vread = [&](int gi, f16x8 (&va)[2]) {
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
                 const uint16_t* vp = &v_lds[(db * 32 + lr) * VPITCH + gi * 16 + 4 * g];
-                const bf16x4 lo = *reinterpret_cast<const bf16x4*>(vp);
-                const bf16x4 hi = *reinterpret_cast<const bf16x4*>(vp + 8);
-                va[db] = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vp);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vp + 8);
+                va[db] = __builtin_bit_cast(f16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
         };
         // groups wholly past ctx hold only masked keys and are skipped; the
         // next group's V^T is read before this group's exponentials
         const int ngroups = (a.ctx + 15) / 16 < 2 * NKB ? (a.ctx + 15) / 16 : 2 * NKB;
-        bf16x8 vcur[2], vnext[2];
+        f16x8 vcur[2], vnext[2];
         vread(0, vcur);
 #pragma unroll
         for (int gi = 0; gi < 2 * NKB; ++gi) {
@@ -188,17 +193,17 @@ __global__ __launch_bounds__(256, 3) void attn_ctx_bf16_kernel(CtxArgs a) {
             uint32_t w[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                w[e] = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[kb][h2 * 8 + 2 * e], a.c, mneg)),
-                                   __builtin_amdgcn_exp2f(fmaf(s[kb][h2 * 8 + 2 * e + 1], a.c, mneg)));
+                w[e] = pack_f16x2(__builtin_amdgcn_exp2f(fmaf(s[kb][h2 * 8 + 2 * e], a.c, mneg)),
+                                  __builtin_amdgcn_exp2f(fmaf(s[kb][h2 * 8 + 2 * e + 1], a.c, mneg)));
             const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3];
-            rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w0), kOnes, rsum, false);
-            rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w1), kOnes, rsum, false);
-            rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w2), kOnes, rsum, false);
-            rsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w3), kOnes, rsum, false);
-            const bf16x8 p = __builtin_bit_cast(bf16x8, u32x4{w0, w1, w2, w3});
+            rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w0), kOnes, rsum, false);
+            rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w1), kOnes, rsum, false);
+            rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w2), kOnes, rsum, false);
+            rsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w3), kOnes, rsum, false);
+            const f16x8 p = __builtin_bit_cast(f16x8, u32x4{w0, w1, w2, w3});
 #pragma unroll
             for (int db = 0; db < 2; ++db) {
-                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[db], p, o[db], 0, 0, 0);
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vcur[db], p, o[db], 0, 0, 0);
                 vcur[db] = vnext[db];
             }
         }

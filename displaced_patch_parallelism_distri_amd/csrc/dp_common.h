@@ -15,6 +15,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // bf16 <-> fp32.  Widening is exact; narrowing is round-to-nearest-even
 // (the compiler emits v_cvt_pk_bf16_f32 on gfx950).
@@ -30,6 +32,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     v.x = (__bf16)lo;
     v.y = (__bf16)hi;
     return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two packed fp32 values -> two f16, round to nearest even (gfx950:
+// v_cvt_pk_f16_f32).  Values beyond the f16 range become +-inf.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    f16x2 v;
+    v.x = (_Float16)lo;
+    v.y = (_Float16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+// A word of two bf16 -> the same two values as f16.  Exact for magnitudes in
+// [2^-14, 65504] and for zero; smaller values round to the f16 subnormal
+// grid (absolute error below 2^-25), larger ones (|v| >= 65536) become inf.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+    return pack_f16x2(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
 }
 
 // Element-type traits for the two storage dtypes: a 16-byte vector holds

@@ -95,9 +95,17 @@ const char *distri_last_error(void);
  * head_dim must be 64 and H*W*heads*head_dim below 2^31
  * (DISTRI_ERR_UNSUPPORTED otherwise).  The bf16 path may split the keys of
  * some query tiles into chunks; the workspace then holds their partial
- * results (its size depends on the current device's compute-unit count).  bf16 inputs are
- * computed with bf16 MFMA and fp32 accumulation / softmax; fp32 inputs in
- * fp32 throughout.
+ * results.  Its size is a function of (g, heads, head_dim, dtype) alone: the
+ * split is planned for a 256-compute-unit MI355X, and the same plan runs
+ * unchanged (in more rounds) on a device with fewer.  The workspace must not
+ * overlap any input or out (DISTRI_ERR_ALIAS).
+ * Arithmetic: fp32 inputs are computed in fp32 throughout.  bf16 inputs: the
+ * scores Q K^T on bf16 MFMA with fp32 accumulation, the softmax in fp32, and
+ * the weighted sum of V on f16 MFMA with fp32 accumulation (the weights
+ * rounded to f16, which keeps their error well inside the output's bf16
+ * rounding).  V is therefore taken as f16: every V element must be finite
+ * with magnitude below 65504 (a larger one becomes inf); elements below
+ * 2^-14 in magnitude are carried with absolute error under 2^-25.
  */
 int distri_patch_self_attn_workspace_size(const distri_patch_geom *g, int64_t heads,
                                           int64_t head_dim, int dtype, size_t *bytes);
@@ -122,7 +130,9 @@ int distri_patch_self_attn(const distri_patch_geom *g, int64_t heads, int64_t he
  * head_dim must be 64 and ctx_len >= 1.  In bf16 with ctx_len <= 128 the
  * whole context of one (image, head) is held on chip and the workspace size
  * is 0; otherwise the self-attention kernels run with L = ctx_len, under the
- * same limits as distri_patch_self_attn.
+ * same limits as distri_patch_self_attn.  Arithmetic and the range of v_ctx
+ * are those of distri_patch_self_attn (f16 weighted sum of V in bf16); the
+ * workspace must not overlap any input or out.
  */
 int distri_patch_cross_attn_workspace_size(const distri_patch_geom *g, int64_t heads,
                                            int64_t head_dim, int64_t ctx_len, int dtype,

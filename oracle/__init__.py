@@ -195,6 +195,22 @@ def cross_attn(scale, q, k_ctx, v_ctx):
     return out
 
 
+def round_to(a, dtype):
+    """Every value rounded to the nearest value of ``dtype``, ties to even,
+    returned as float64: "bf16" keeps 8 significant bits (the upper half of
+    an IEEE binary32), "f32" is binary32.  This is storage rounding, applied
+    where a chain of ops hands a tensor of that dtype to the next op (bf16
+    results of these ops stay far inside binary32's exponent range, so bf16
+    subnormals and overflow are not handled)."""
+    a = _f64(a)
+    if dtype == "f32":
+        return a.astype(np.float32).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    m, e = np.frexp(a)                       # a = m 2^e with 0.5 <= |m| < 1
+    return np.ldexp(np.rint(np.ldexp(m, 8)), e - 8)   # np.rint: ties to even
+
+
 def silu(z):
     """Elementwise z / (1 + exp(-z)), float64, same shape."""
     zf = _f64(z)
@@ -214,8 +230,18 @@ def silu(z):
 # [C,C], b_o.  A state is a dict of the previous step's context: gn1, gn2
 # [B, n, G, 2] moment tables, conv_in [B, H, W, C] (g1 of every patch), k, v
 # [B, H*W, C].  These functions only sequence the C routines above.
+#
+# ``act_dtype``: None chains the ops in float64 throughout.  "bf16" or "f32"
+# gives every op its inputs as tensors of that dtype, as a chain of the
+# library's ops holds them: each op's result is rounded (round_to) before the
+# next op reads it, and the results returned (y and the new state rows) are
+# each op's own result before that rounding.
 
-def patch_block(geom, wts, x, state):
+def _rounder(act_dtype):
+    return (lambda a: a) if act_dtype is None else (lambda a: round_to(a, act_dtype))
+
+
+def patch_block(geom, wts, x, state, act_dtype=None):
     """One asynchronous step for patch i: x [B, h, W, C] -> (y [B, Lq, C],
     new state).  Stale reads come from ``state``; the new state is a copy
     with patch i's rows / slots replaced by this step's fresh values (README
@@ -223,17 +249,18 @@ def patch_block(geom, wts, x, state):
     B, H, W, n, i = geom
     C, G, nh = wts["channels"], wts["groups"], wts["heads"]
     h, Lq, L, d = H // n, (H // n) * W, H * W, C // nh
+    r = _rounder(act_dtype)
     z1, fm1 = async_groupnorm(geom, C, G, wts["eps"], x, state["gn1"], wts["gn1_gamma"],
                               wts["gn1_beta"])
     g1 = silu(z1)
-    hh = patch_conv3x3_halo(geom, C, C, g1, state["conv_in"], wts["conv_w"], wts["conv_b"])
-    n2, fm2 = async_groupnorm(geom, C, G, wts["eps"], hh, state["gn2"], wts["gn2_gamma"],
+    hh = patch_conv3x3_halo(geom, C, C, r(g1), state["conv_in"], wts["conv_w"], wts["conv_b"])
+    n2, fm2 = async_groupnorm(geom, C, G, wts["eps"], r(hh), state["gn2"], wts["gn2_gamma"],
                               wts["gn2_beta"])
-    q, k, v, ks, vs = patch_qkv_proj(geom, C, n2, wts["w_qkv"], wts["b_qkv"], state["k"], state["v"])
-    o = patch_self_attn(geom, nh, d, wts["scale"], q.reshape(B, Lq, nh, d), k.reshape(B, Lq, nh, d),
-                        v.reshape(B, Lq, nh, d), _f64(state["k"]).reshape(B, L, nh, d),
-                        _f64(state["v"]).reshape(B, L, nh, d))
-    y = linear(o.reshape(B, Lq, C), wts["w_o"], wts["b_o"])
+    q, k, v, ks, vs = patch_qkv_proj(geom, C, r(n2), wts["w_qkv"], wts["b_qkv"], state["k"], state["v"])
+    o = patch_self_attn(geom, nh, d, wts["scale"], r(q).reshape(B, Lq, nh, d),
+                        r(k).reshape(B, Lq, nh, d), r(v).reshape(B, Lq, nh, d),
+                        _f64(state["k"]).reshape(B, L, nh, d), _f64(state["v"]).reshape(B, L, nh, d))
+    y = linear(r(o).reshape(B, Lq, C), wts["w_o"], wts["b_o"])
     tgeom = (B, n, 1, n, i)
     new = {
         "gn1": refresh_stale(tgeom, 2 * G, fm1.reshape(B, 1, 2 * G),
@@ -248,7 +275,7 @@ def patch_block(geom, wts, x, state):
     return y, new
 
 
-def patch_block_sync(geom, wts, x_full):
+def patch_block_sync(geom, wts, x_full, act_dtype=None):
     """The synchronous (warm-up) step for all n patches: each stage runs for
     every patch, and its fresh values are shared, before any patch reads
     them in the next stage (the first denoising steps exchange activations
@@ -257,6 +284,7 @@ def patch_block_sync(geom, wts, x_full):
     B, H, W, n, _ = geom
     C, G, nh = wts["channels"], wts["groups"], wts["heads"]
     h, Lq, L, d = H // n, (H // n) * W, H * W, C // nh
+    r = _rounder(act_dtype)
     xf = _f64(x_full)
     geoms = [(B, H, W, n, j) for j in range(n)]
     rows = [slice(j * h, (j + 1) * h) for j in range(n)]
@@ -273,24 +301,24 @@ def patch_block_sync(geom, wts, x_full):
         conv_in = refresh_stale(geoms[j], W * C, g1[j].reshape(B, h, W * C),
                                 conv_in.reshape(B, H, W * C))
     conv_in = conv_in.reshape(B, H, W, C)
-    hh = [patch_conv3x3_halo(geoms[j], C, C, g1[j], conv_in, wts["conv_w"], wts["conv_b"])
+    hh = [r(patch_conv3x3_halo(geoms[j], C, C, r(g1[j]), r(conv_in), wts["conv_w"], wts["conv_b"]))
           for j in range(n)]
     gn2 = np.zeros((B, n, G, 2))
     for j in range(n):
         gn2[:, j] = group_moments(hh[j], G)
-    n2 = [async_groupnorm(geoms[j], C, G, eps, hh[j], gn2, wts["gn2_gamma"], wts["gn2_beta"])[0]
+    n2 = [r(async_groupnorm(geoms[j], C, G, eps, hh[j], gn2, wts["gn2_gamma"], wts["gn2_beta"])[0])
           for j in range(n)]
     kmap = np.zeros((B, L, C))
     vmap = np.zeros((B, L, C))
     qkv = []
     for j in range(n):
         q, k, v, kmap, vmap = patch_qkv_proj(geoms[j], C, n2[j], wts["w_qkv"], wts["b_qkv"], kmap, vmap)
-        qkv.append((q, k, v))
+        qkv.append((r(q), r(k), r(v)))
     y = np.zeros((B, L, C))
     for j in range(n):
         q, k, v = (t.reshape(B, Lq, nh, d) for t in qkv[j])
-        o = patch_self_attn(geoms[j], nh, d, wts["scale"], q, k, v, kmap.reshape(B, L, nh, d),
-                            vmap.reshape(B, L, nh, d))
-        y[:, toks[j]] = linear(o.reshape(B, Lq, C), wts["w_o"], wts["b_o"])
+        o = patch_self_attn(geoms[j], nh, d, wts["scale"], q, k, v, r(kmap).reshape(B, L, nh, d),
+                            r(vmap).reshape(B, L, nh, d))
+        y[:, toks[j]] = linear(r(o).reshape(B, Lq, C), wts["w_o"], wts["b_o"])
     state = {"gn1": gn1, "conv_in": conv_in, "gn2": gn2, "k": kmap, "v": vmap}
     return y, state

@@ -1,19 +1,29 @@
 """Helpers shared by the GPU parity tests: seeded inputs on both sides,
 oracle references, and the tolerance rule.
 
-Tolerance (written once, used by every parity test).  For every element x of
-the oracle output (fp64) and the kernel output y in the output dtype:
+Tolerance (written once, used by every parity test).  With x the oracle
+output (fp64) and y the kernel output in the output dtype, over the whole
+output tensor (or the sampled rows of a full-size case):
 
-    |y - x| <= tol * RMS(oracle output) + half_ulp(x)
+    max |y - x| <= tol * RMS(x)
     tol = 2e-2 for bf16 inputs (fp32 accumulation), 1e-4 for fp32 inputs
 
-The stated bound applies to the computation; half_ulp(x) is the rounding of
-the exact value to the output dtype, which every kernel that returns that
-dtype incurs (for bf16, 2^-8 |x| at most).  Without it no bf16-output
-implementation can meet the bound on attention: there the exact result
-rounded once to bf16 already sits at 0.0184-0.0188 x RMS on the 1024^2
-level-3 workload (heavy-tailed outputs reach 8-9 x RMS).  The plain
-max|y - x| / RMS is reported alongside.
+The bound includes the output's own rounding to its dtype.  Each case first
+computes, from the oracle alone, its rounding floor F = max |rnd(x) - x| /
+RMS(x), rnd = round to nearest even in the output dtype: the score of the
+best output that dtype can hold.  Heavy-tailed outputs spend most of the
+bound on it (attention: F = 0.017-0.019).  Where F <= tol the bound above is
+the rule, unchanged.  Where F > tol no output in that dtype can meet it (the
+SiLU form of GroupNorm: F = 0.026; short-context cross-attention: F up to
+0.022); there every element must lie within the bound or be the correctly
+rounded value of x:
+
+    |y - x| <= max(tol * RMS(x), half_ulp(x) + 2^-12 |x|)  for every element
+
+(2^-12 |x| admits the other neighbour when x lies that close to a rounding
+midpoint, the size of the kernels' own arithmetic error).  Each comparison
+prints max|y - x| / RMS and F, and appends them to $PARITY_REPORT when that is
+set.
   GroupNorm fresh moments: |d m1| <= 1e-5 sqrt(m2) + 1e-7, |d m2| <= 1e-5 m2 + 1e-7
   refresh: bitwise.
 """
@@ -47,24 +57,42 @@ def half_ulp(x, dtype):
     return np.where(a > 0, np.ldexp(1.0, e - 1 - bits), 0.0)
 
 
+def rounding_floor(ref, dtype):
+    """max |rnd(x) - x| / RMS(x): the score of the correctly rounded output."""
+    ref = np.asarray(ref, dtype=np.float64)
+    rms = max(float(np.sqrt(np.mean(ref * ref))), 1e-30)
+    return float(np.max(np.abs(oracle.round_to(ref, dtype) - ref))) / rms
+
+
 def assert_close(got, ref, dtype, what):
+    """The parity rule above; returns max|got - ref| / RMS(ref)."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert np.all(np.isfinite(got)), f"{what}: non-finite output"
     rms = max(float(np.sqrt(np.mean(ref * ref))), 1e-30)
+    tol = TOL[dtype]
     err = np.abs(got - ref)
-    excess = err - (TOL[dtype] * rms + half_ulp(ref, dtype))
-    worst = np.unravel_index(int(np.argmax(excess)), excess.shape)
-    plain = float(err.max()) / rms
-    arith = float(np.max(err - half_ulp(ref, dtype))) / rms
+    rel = float(err.max()) / rms
+    floor = rounding_floor(ref, dtype)
+    print(f"parity {what}: max|err|/RMS = {rel:.4e} (bound {tol:.0e}; rounding floor {floor:.4e})",
+          flush=True)
     report = os.environ.get("PARITY_REPORT")
     if report:
         with open(report, "a") as f:
-            f.write(json.dumps({"case": what, "dtype": dtype, "max_err_over_rms": plain,
-                                "arith_err_over_rms": arith, "n": int(err.size)}) + "\n")
-    assert excess[worst] <= 0, (f"{what}: |err| exceeds {TOL[dtype]} x RMS + half ulp at {worst}: "
-                                f"got {got[worst]}, oracle {ref[worst]}; max|err|/rms = {plain:.3e}")
-    return plain, arith
+            f.write(json.dumps({"case": what, "dtype": dtype, "max_err_over_rms": rel, "bound": tol,
+                                "rounding_floor": floor, "n": int(err.size)}) + "\n")
+    if floor <= tol:
+        worst = np.unravel_index(int(np.argmax(err)), err.shape)
+        assert rel <= tol, (f"{what}: max|err| = {rel:.4e} x RMS exceeds {tol} x RMS at {worst}: "
+                            f"got {got[worst]}, oracle {ref[worst]}")
+    else:
+        allow = np.maximum(tol * rms, half_ulp(ref, dtype) + np.ldexp(np.abs(ref), -12))
+        excess = err - allow
+        worst = np.unravel_index(int(np.argmax(excess)), err.shape)
+        assert excess[worst] <= 0, (f"{what}: rounding floor {floor:.4e} > {tol}, and the element at "
+                                    f"{worst} is neither within {tol} x RMS nor correctly rounded: "
+                                    f"got {got[worst]}, oracle {ref[worst]}")
+    return rel
 
 
 def to_np(t):

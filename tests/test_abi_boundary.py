@@ -77,6 +77,43 @@ def test_attention_empty_output_is_ok_without_pointers(lib):
     assert attn(lib, (2, 0, 64, 8, 0), ptrs=[None] * 6) == OK
 
 
+def test_attention_workspace_size_needs_no_device(lib):
+    """The key-split plan is made for a fixed 256-CU machine, so the size is a
+    function of the sizes alone (and nonzero where tasks are split)."""
+    g = (2, 240, 240, 8, 4)
+    n = dp.distri_patch_self_attn_workspace_size(g, 10, 64, BF16)
+    # 44 leftover tasks x 17 key chunks x 512 queries x (64 + 2) fp32
+    assert n == 44 * 17 * 512 * 66 * 4
+    assert dp.distri_patch_self_attn_workspace_size(g, 10, 64, F32) == 0
+    assert n == dp.distri_patch_self_attn_workspace_size(g, 10, 64, BF16)
+
+
+def test_attention_rejects_small_or_overlapping_workspace(lib):
+    g = (2, 240, 240, 8, 4)
+    need = dp.distri_patch_self_attn_workspace_size(g, 10, 64, BF16)
+    full = 2 * 240 * 240 * 640 * 2
+    p = [A + k * 4 * full for k in range(6)]
+    ws = A + 24 * full
+    assert attn(lib, g, ptrs=p, ws=None, wsb=0) == WS
+    assert attn(lib, g, ptrs=p, ws=ws, wsb=need - 16) == WS
+    assert attn(lib, g, ptrs=p, ws=ws + 8, wsb=need) == ALIGN
+    for k in range(6):                       # q, k_fresh, v_fresh, k_stale, v_stale, out
+        assert attn(lib, g, ptrs=p, ws=p[k] + 256, wsb=need) == ALIAS, k
+
+
+def test_cross_attention_rejects_overlapping_workspace(lib):
+    g = (2, 64, 64, 8, 3)
+    ctx = 300                                # past the on-chip context: a workspace is needed
+    need = dp.distri_patch_cross_attn_workspace_size(g, 10, ctx, BF16)
+    assert need > 0
+    p = [A + k * 64 * MB for k in range(4)]  # q, k_ctx, v_ctx, out
+    for k in range(4):
+        st = lib.distri_patch_cross_attn(G(*g), 10, 64, ctx, 0.125, BF16, *p, p[k] + 256, need, None)
+        assert st == ALIAS, k
+    st = lib.distri_patch_cross_attn(G(*g), 10, 64, ctx, 0.125, BF16, *p, A + 8 * 64 * MB, need - 16, None)
+    assert st == WS
+
+
 def conv(lib, geom, cin=640, cout=640, dtype=BF16, ptrs=None, bias=None):
     p = ptrs or [A + k * 256 * MB for k in range(4)]
     return lib.distri_patch_conv3x3_halo(G(*geom), cin, cout, dtype, p[0], p[1], p[2], bias, p[3], None)

@@ -3,7 +3,9 @@ Q/K/V projection with the K/V refresh -> attention -> output projection) and
 of the two GroupNorm forms it adds (SiLU epilogue, moments into the table),
 through the C ABI, against the CPU oracle on the same seeded inputs
 (tolerance rule in tests/parity_util.py; the block is compared at its output
-and at every state map it writes).
+and at every state map it writes).  The oracle's block is given act_dtype =
+the workload dtype: each op reads its inputs as tensors of that dtype, as the
+library's chain of ops does, and each op's own result is compared.
 """
 import numpy as np
 import pytest
@@ -121,7 +123,7 @@ def test_block_async_step(wl, patch):
     st_in = _gpu_state(d["state"])
     st_out = _gpu_state(d["state"])
     y = _run_block(wl, d, x, st_in, st_out)
-    ref_y, ref_st = oracle.patch_block(wl.geom, wts, x_cpu, d["state"])
+    ref_y, ref_st = oracle.patch_block(wl.geom, wts, x_cpu, d["state"], act_dtype=wl.dtype)
     tag = f"block {wl.name} patch {patch}"
     assert_close(to_np(y), ref_y, wl.dtype, tag)
     _compare_state(wl, st_out, ref_st, d["state"], tag)
@@ -149,7 +151,7 @@ def test_block_warmup_then_async_step(wl):
     y_sync = dp.distri_patch_block_sync(wl.geom, {k: v.cuda() for k, v in d["weights"].items()},
                                         xp_patches, st, groups=wl.groups, heads=wl.heads, eps=wl.eps,
                                         scale=wl.head_dim ** -0.5)
-    ref_sync, ref_st = oracle.patch_block_sync(wl.geom, wts, xp)
+    ref_sync, ref_st = oracle.patch_block_sync(wl.geom, wts, xp, act_dtype=wl.dtype)
     got = to_np(y_sync).transpose(1, 0, 2, 3).reshape(B, n * Lq, C)
     assert_close(got, ref_sync, wl.dtype, f"block sync {wl.name}")
     for key in ("conv_in", "k", "v"):
@@ -160,7 +162,11 @@ def test_block_warmup_then_async_step(wl):
     i = wl.patch
     x_cpu = d["x"][:, i * h:(i + 1) * h].contiguous()
     y = _run_block(wl, d, x_cpu.cuda(), st)
-    ref_y, _ = oracle.patch_block(wl.geom, wts, x_cpu, ref_st)
+    # step 2 reads the state as the library holds it: maps in the activation
+    # dtype, moment tables in fp32
+    held = {k: oracle.round_to(v, wl.dtype if k in ("conv_in", "k", "v") else "f32")
+            for k, v in ref_st.items()}
+    ref_y, _ = oracle.patch_block(wl.geom, wts, x_cpu, held, act_dtype=wl.dtype)
     assert_close(to_np(y), ref_y, wl.dtype, f"block step 2 {wl.name}")
 
 

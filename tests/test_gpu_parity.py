@@ -38,8 +38,9 @@ FULL_CASES = [(W["tiny"], 0), (W["tiny"], 1), (W["sdxl1024_l2"], 0), (W["sdxl102
               (W["sdxl1024_l2"], 7), (W["sdxl1024_l3"], 1), (W["sdxl1024_l3"], 3),
               (RAGGED_BF16, 0), (RAGGED_BF16, 2), (RAGGED_BF16, 3), (RAGGED_F32, 1),
               (TINY_L_BF16, 1), (TAIL_BF16, 0)]
-SAMPLED_CASES = [(W["sdxl2048_l2"], 4), (W["sdxl3840_l2"], 0), (W["sdxl3840_l2"], 4),
-                 (W["sdxl3840_l2"], 7), (W["sdxl3840_l3"], 4)]
+SAMPLED_CASES = [(W["sdxl2048_l2"], 0), (W["sdxl2048_l2"], 4), (W["sdxl2048_l2"], 7),
+                 (W["sdxl3840_l2"], 0), (W["sdxl3840_l2"], 4), (W["sdxl3840_l2"], 7),
+                 (W["sdxl3840_l3"], 0), (W["sdxl3840_l3"], 4), (W["sdxl3840_l3"], 7)]
 
 
 def _ids(cases):
@@ -285,3 +286,17 @@ def test_groupnorm_reused_workspace_is_exact():
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)), f"call {k}"
         assert torch.equal(fm, ref_fm), f"call {k}"
+
+
+@pytest.mark.parametrize("v_scale", [2.0 ** 12, 2.0 ** -10], ids=["v_x4096", "v_x2^-10"])
+def test_attention_value_range(v_scale):
+    """The weighted sum of V runs in f16: V far above and below unit scale
+    (|v| up to about 2e4, and down into f16's subnormal range) still meets
+    the bound."""
+    wl = W["sdxl1024_l3"].with_patch(2)
+    d = dict(cpu_inputs(wl))
+    for k in ("v_fresh", "v_stale"):
+        d[k] = (d[k].float() * v_scale).to(torch.bfloat16)
+    g = gpu_copy(d)
+    assert_close(to_np(_run_attention(wl, g)), _oracle_attention(wl, d), "bf16",
+                 f"attention V x {v_scale:g}")

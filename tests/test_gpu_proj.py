@@ -109,8 +109,10 @@ def test_proj_full_size_sampled(wl, patch):
 
 def test_attention_layer_chain():
     """Q/K/V projection (refreshing the stale maps) -> attention over the
-    fresh + stale K/V -> output projection, against the oracle's chain in
-    fp64 (the GPU rounds every intermediate to bf16)."""
+    fresh + stale K/V -> output projection, against the oracle's chain fed,
+    like the library's, with each op's result rounded to the activation dtype
+    (q, k, v, the refreshed stale maps and the attention output are bf16
+    tensors); each op's own result is compared."""
     wl = W["sdxl1024_l2"].with_patch(3)
     d = si.make_proj_inputs(wl)
     g = {k: v.cuda() for k, v in d.items()}
@@ -125,8 +127,10 @@ def test_attention_layer_chain():
     rq, rk, rv, rks, rvs = oracle.patch_qkv_proj(wl.geom, wl.channels, d["x"], d["w_qkv"], d["b_qkv"],
                                                  d["k_stale"], d["v_stale"])
     sh = (B, Lq, nh, hd)
-    ro = oracle.patch_self_attn(wl.geom, nh, hd, hd ** -0.5, rq.reshape(sh), rk.reshape(sh),
-                                rv.reshape(sh), rks.reshape(B, L, nh, hd), rvs.reshape(B, L, nh, hd))
-    ry = oracle.linear(ro.reshape(B, Lq, nh * hd), d["w_o"], d["b_o"])
+    r = lambda a: oracle.round_to(a, wl.dtype)
+    ro = oracle.patch_self_attn(wl.geom, nh, hd, hd ** -0.5, r(rq).reshape(sh), r(rk).reshape(sh),
+                                r(rv).reshape(sh), r(rks).reshape(B, L, nh, hd),
+                                r(rvs).reshape(B, L, nh, hd))
+    ry = oracle.linear(r(ro).reshape(B, Lq, nh * hd), d["w_o"], d["b_o"])
     assert_close(to_np(o).reshape(B, Lq, -1), ro.reshape(B, Lq, -1), wl.dtype, "chain attention")
     assert_close(to_np(y), ry, wl.dtype, "chain out_proj")

@@ -9,7 +9,10 @@ against checks that do not reuse it:
 * an asynchronous step whose stale state is the synchronous step's own
   state on the same input (stale = fresh) gives the same rows again;
 * the asynchronous step changes only patch i's rows / slots of the state, and
-  those hold its own fresh values.
+  those hold its own fresh values;
+* with act_dtype = "bf16" (every op fed bf16 tensors) the n = 1 block and the
+  synchronous step equal torch's fp64 library block with the same tensors
+  rounded to bf16 by a bit-level round-to-nearest-even written here.
 """
 import numpy as np
 import pytest
@@ -34,21 +37,33 @@ def _state(d):
     return {k: v.double().numpy() for k, v in d["state"].items()}
 
 
-def _torch_block(wl, w, x):
-    """Full-image block with torch fp64 library layers; x [B, H, W, C]."""
+def _bits_rne_bf16(a):
+    """float64 tensor -> nearest bf16 value (8 significant bits), ties to
+    even, by integer arithmetic on the binary64 encoding: drop the low 45 of
+    its 52 fraction bits after adding half of that unit (minus one, plus the
+    lowest kept bit, which breaks ties to even)."""
+    b = a.contiguous().view(torch.int64)
+    keep = (b >> 45) & 1
+    b = (b + ((1 << 44) - 1) + keep) & ~((1 << 45) - 1)
+    return b.view(torch.float64)
+
+
+def _torch_block(wl, w, x, rnd=lambda a: a):
+    """Full-image block with torch fp64 library layers; x [B, H, W, C].
+    ``rnd`` is applied to each layer's result that the next layer reads."""
     B, H, W, C = x.shape
     nh, d = wl.heads, C // wl.heads
     t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
     xc = t(x).permute(0, 3, 1, 2)
-    z = F.silu(F.group_norm(xc, wl.groups, t(w["gn1_gamma"]), t(w["gn1_beta"]), wl.eps))
+    z = rnd(F.silu(F.group_norm(xc, wl.groups, t(w["gn1_gamma"]), t(w["gn1_beta"]), wl.eps)))
     wc = t(w["conv_w"]).permute(0, 3, 1, 2)  # [Cout, Cin, 3, 3]
-    hh = F.conv2d(z, wc, t(w["conv_b"]), padding=1)
-    n2 = F.group_norm(hh, wl.groups, t(w["gn2_gamma"]), t(w["gn2_beta"]), wl.eps)
+    hh = rnd(F.conv2d(z, wc, t(w["conv_b"]), padding=1))
+    n2 = rnd(F.group_norm(hh, wl.groups, t(w["gn2_gamma"]), t(w["gn2_beta"]), wl.eps))
     tok = n2.permute(0, 2, 3, 1).reshape(B, H * W, C)
-    qkv = F.linear(tok, t(w["w_qkv"]), t(w["b_qkv"]))
+    qkv = rnd(F.linear(tok, t(w["w_qkv"]), t(w["b_qkv"])))
     q, k, v = (a.reshape(B, H * W, nh, d).transpose(1, 2) for a in qkv.split(C, dim=-1))
     p = torch.softmax(q @ k.transpose(-1, -2) * w["scale"], dim=-1)
-    o = (p @ v).transpose(1, 2).reshape(B, H * W, C)
+    o = rnd((p @ v).transpose(1, 2).reshape(B, H * W, C))
     return F.linear(o, t(w["w_o"]), t(w["b_o"])).numpy()
 
 
@@ -62,6 +77,33 @@ def test_single_patch_block_is_the_library_block():
     y, _ = oracle.patch_block(full.geom, w, x, _state(d))
     ref = _torch_block(full, w, x)
     np.testing.assert_allclose(y, ref, rtol=1e-9, atol=1e-10)
+
+
+def test_bit_rounding_helper():
+    x = torch.tensor([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -8 + 2.0 ** -30, -3.1, 0.0],
+                     dtype=torch.float64)
+    want = [1.0, 1 + 2.0 ** -6, 1 + 2.0 ** -7, -3.09375, 0.0]
+    assert _bits_rne_bf16(x).tolist() == want
+    y = torch.randn(10000, dtype=torch.float32).double()   # binary32 values: one rounding
+    assert torch.equal(_bits_rne_bf16(y), y.float().to(torch.bfloat16).double())
+
+
+def test_block_with_bf16_tensors_is_the_rounded_library_block():
+    wl = SMALL
+    full = si.Workload(wl.name, wl.batch, wl.channels, wl.height, wl.width, 1, wl.heads,
+                       groups=wl.groups, dtype="f32", seed=wl.seed)
+    d = si.make_block_inputs(full)
+    w = _wts(full, d)
+    x = d["x"].double().numpy()
+    ref = _torch_block(full, w, x, _bits_rne_bf16)
+    y, _ = oracle.patch_block(full.geom, w, x, _state(d), act_dtype="bf16")
+    np.testing.assert_allclose(y, ref, rtol=1e-9, atol=1e-10)
+    assert not np.allclose(y, _torch_block(full, w, x), rtol=1e-5, atol=1e-6)
+    d4 = si.make_block_inputs(wl)
+    y_sync, _ = oracle.patch_block_sync(wl.geom, _wts(wl, d4), d4["x"].double().numpy(),
+                                        act_dtype="bf16")
+    np.testing.assert_allclose(y_sync, _torch_block(wl, _wts(wl, d4), d4["x"].double().numpy(),
+                                                    _bits_rne_bf16), rtol=1e-9, atol=1e-10)
 
 
 def test_sync_step_reproduces_the_full_image_block():
