@@ -24,6 +24,7 @@ __all__ = [
     "distri_patch_block_sync", "distri_patch_block_workspace_size",
     "distri_patch_block_sync_workspace_size", "BlockWeights", "BlockState",
     "distri_patch_cross_attn", "distri_patch_cross_attn_workspace_size", "naive_geom",
+    "distri_async_groupnorm_noalloc",
     "DISTRI_F32", "DISTRI_BF16",
 ]
 
@@ -40,7 +41,8 @@ SYMBOLS = ("distri_abi_version", "distri_status_str", "distri_last_error",
            "distri_patch_out_proj", "distri_async_groupnorm_silu", "distri_group_moments",
            "distri_patch_block_workspace_size", "distri_patch_block",
            "distri_patch_block_sync_workspace_size", "distri_patch_block_sync",
-           "distri_patch_cross_attn_workspace_size", "distri_patch_cross_attn")
+           "distri_patch_cross_attn_workspace_size", "distri_patch_cross_attn",
+           "distri_async_groupnorm_noalloc")
 
 
 class DistriError(RuntimeError):
@@ -94,6 +96,7 @@ def load():
     lib.distri_patch_qkv_proj.argtypes = [G, I64, I] + [P] * 9
     lib.distri_patch_out_proj.argtypes = [G, I64, I] + [P] * 5
     lib.distri_async_groupnorm_silu.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 7 + [SZ, P]
+    lib.distri_async_groupnorm_noalloc.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 6 + [P]
     lib.distri_group_moments.argtypes = [G, I64, I64, I, P, P, P, SZ, P]
     BW, BS = ctypes.POINTER(BlockWeights), ctypes.POINTER(BlockState)
     lib.distri_patch_block_workspace_size.argtypes = [G, BW, I, ctypes.POINTER(SZ)]
@@ -266,6 +269,27 @@ def distri_async_groupnorm(g, groups, x_fresh, stale_moments, gamma=None, beta=N
     [B,n,G,2] fp32 -> (y [B,h,W,C], fresh_moments [B,G,2] fp32)."""
     return _groupnorm("distri_async_groupnorm", g, groups, x_fresh, stale_moments, gamma, beta,
                       eps, y, fresh_moments, workspace, stream)
+
+
+def distri_async_groupnorm_noalloc(g, groups, x_fresh, stale_moments, gamma=None, beta=None,
+                                   eps=1e-5, y=None, fresh_moments=None, stream=None):
+    """distri_async_groupnorm without a workspace (the library's own 2 MiB
+    device scratch; calls that overlap on one GPU race)."""
+    g = _as_geom(g)
+    code = _dtype_code(x_fresh)
+    C = x_fresh.shape[-1]
+    if y is None:
+        y = _new(stream, x_fresh.shape, x_fresh)
+    if fresh_moments is None:
+        fresh_moments = _new(stream, (g.batch, groups, 2), x_fresh, torch.float32)
+    st = load().distri_async_groupnorm_noalloc(
+        ctypes.byref(g), C, groups, float(eps), code, _ptr(x_fresh, "x_fresh", x_fresh.dtype),
+        _ptr(stale_moments, "stale_moments", torch.float32, g.batch * g.n_patches * groups * 2),
+        _ptr(gamma, "gamma", torch.float32, C), _ptr(beta, "beta", torch.float32, C),
+        _ptr(y, "y", x_fresh.dtype, x_fresh.numel()),
+        _ptr(fresh_moments, "fresh_moments", torch.float32, g.batch * groups * 2), _stream(stream))
+    _check(st, "distri_async_groupnorm_noalloc")
+    return y, fresh_moments
 
 
 def distri_async_groupnorm_silu(g, groups, x_fresh, stale_moments, gamma=None, beta=None,

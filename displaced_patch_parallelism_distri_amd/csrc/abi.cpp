@@ -27,10 +27,13 @@ using namespace dp_abi;
 
 namespace {
 
+// use_scratch: the allocation-free form, whose workspace is the library's
+// own scratch array (workspace / workspace_bytes ignored).
 int groupnorm_entry(int mode, const distri_patch_geom* g, int64_t channels, int64_t groups,
                     float eps, int dtype, const void* x_fresh, const float* stale_moments,
                     const float* gamma, const float* beta, void* y, float* fresh_moments,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    bool use_scratch = false) {
     int st = check_gn_shape(g, channels, groups, dtype);
     if (st) return st;
     DP_CHECK(std::isfinite(eps) && eps >= 0.f, DISTRI_ERR_SHAPE, "eps must be finite and >= 0");
@@ -44,9 +47,16 @@ int groupnorm_entry(int mode, const distri_patch_geom* g, int64_t channels, int6
                  aligned16(beta) && aligned16(y) && aligned16(fresh_moments),
              DISTRI_ERR_ALIGN, "tensor pointers must be 16-byte aligned");
     const size_t need = dp::groupnorm_workspace_bytes(gg, channels, groups, int(eb));
-    DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
-             "groupnorm workspace missing or too small");
-    DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (use_scratch) {
+        DP_CHECK(need <= dp::kGnScratchBytes, DISTRI_ERR_UNSUPPORTED,
+                 "this shape needs more GroupNorm scratch than the 2 MiB the allocation-free form "
+                 "holds: use distri_async_groupnorm with a workspace");
+        workspace = nullptr;  // not an argument of this form; no overlap to check
+    } else {
+        DP_CHECK(workspace != nullptr && workspace_bytes >= need, DISTRI_ERR_WORKSPACE,
+                 "groupnorm workspace missing or too small");
+        DP_CHECK(aligned16(workspace), DISTRI_ERR_ALIGN, "workspace must be 16-byte aligned");
+    }
     const size_t table = size_t(gg.B * gg.n * groups * 2) * 4;
     const size_t fm = size_t(gg.B * groups * 2) * 4;
     const size_t cb = size_t(channels) * 4;
@@ -59,6 +69,10 @@ int groupnorm_entry(int mode, const distri_patch_geom* g, int64_t channels, int6
     DP_CHECK(!overlaps(outs[0], outs[1]) && !overlaps(outs[0], outs[2]) &&
                  !overlaps(outs[1], outs[2]),
              DISTRI_ERR_ALIAS, "outputs overlap each other");
+    if (use_scratch) {
+        const hipError_t e = dp::groupnorm_scratch(&workspace);
+        if (e != hipSuccess) return hip_status(e);
+    }
     return hip_status(dp::launch_groupnorm(gg, channels, groups, eps, dtype == DISTRI_BF16, mode,
                                            x_fresh, stale_moments, gamma, beta, y, fresh_moments,
                                            groups * 2, workspace,
@@ -245,6 +259,15 @@ int distri_async_groupnorm(const distri_patch_geom* g, int64_t channels, int64_t
     return groupnorm_entry(dp::kGnNormalize, g, channels, groups, eps, dtype, x_fresh,
                            stale_moments, gamma, beta, y, fresh_moments, workspace,
                            workspace_bytes, stream);
+}
+
+int distri_async_groupnorm_noalloc(const distri_patch_geom* g, int64_t channels, int64_t groups,
+                                   float eps, int dtype, const void* x_fresh,
+                                   const float* stale_moments, const float* gamma,
+                                   const float* beta, void* y, float* fresh_moments, void* stream) {
+    return groupnorm_entry(dp::kGnNormalize, g, channels, groups, eps, dtype, x_fresh,
+                           stale_moments, gamma, beta, y, fresh_moments, nullptr, 0, stream,
+                           true);
 }
 
 int distri_async_groupnorm_silu(const distri_patch_geom* g, int64_t channels, int64_t groups,

@@ -141,6 +141,10 @@ hipError_t launch_refresh(const Geom& g, int64_t row_elems, int elem_bytes, cons
                           void* stale, hipStream_t s);
 
 size_t groupnorm_workspace_bytes(const Geom& g, int64_t C, int64_t G, int elem_bytes);
+// The GroupNorm scratch array of the allocation-free entry point: its size,
+// and its address on the current device (looked up once per device).
+constexpr size_t kGnScratchBytes = size_t(2) << 20;
+hipError_t groupnorm_scratch(void** ptr);
 // mode: plain normalise, normalise then SiLU, or moments only (y, the
 // stale table and gamma / beta unused).  fresh_moments[b * fm_stride + 2g
 // + {0, 1}] receives (E[x], E[x^2]) of image b, group g over the slice.

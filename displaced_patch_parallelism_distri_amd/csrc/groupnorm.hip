@@ -31,8 +31,18 @@
 // same XCD in both passes and the slice is tens of MB.
 #include "dp_common.h"
 
+#include <mutex>
 
 namespace dp {
+
+// Scratch of the allocation-free entry point (distri_async_groupnorm_noalloc):
+// the chunk sums and per-channel affine that the other entry points keep in
+// a caller's workspace.  One copy per device, alive until the process ends;
+// host code reaches it only through the address hipGetSymbolAddress returns
+// for the current device (groupnorm_scratch).  Nothing in it must start at
+// zero: every value is written before it is read within a call.
+static __device__ __align__(256) unsigned char scratch[kGnScratchBytes];
+
 namespace {
 
 constexpr int kTargetBlocks = 256;
@@ -375,6 +385,27 @@ hipError_t run(const Geom& g, int64_t C, int64_t G, float eps, int mode, const v
 
 size_t groupnorm_workspace_bytes(const Geom& g, int64_t C, int64_t G, int elem_bytes) {
     return workspace_bytes(g, plan_gn(g, C, elem_bytes), C, G);
+}
+
+hipError_t groupnorm_scratch(void** ptr) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        // once per device, with that device current: each device holds its
+        // own copy of the array at its own address
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 hipError_t launch_groupnorm(const Geom& g, int64_t C, int64_t G, float eps, bool bf16, int mode,

@@ -197,6 +197,29 @@ int distri_async_groupnorm(const distri_patch_geom *g, int64_t channels, int64_t
                            size_t workspace_bytes, void *stream);
 
 /*
+ * distri_async_groupnorm_noalloc - distri_async_groupnorm for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  It takes no workspace and calls
+ * no allocating routine; the caller still passes every input and output,
+ * with the same arguments, layouts, limits and results as
+ * distri_async_groupnorm (the same kernels run).
+ *
+ * Its scratch is a static device array of 2 MiB that the library holds on
+ * each device it runs on until the process ends (its address is looked up
+ * once per device, at the first call with that device current).  A shape
+ * whose scratch need (distri_async_groupnorm_workspace_size()) exceeds 2 MiB
+ * returns DISTRI_ERR_UNSUPPORTED with nothing enqueued; the SDXL shapes need
+ * at most a few hundred KB.  Every call on one device shares that device's
+ * array and leaves its contents behind (nothing in it needs clearing): calls
+ * that overlap on one device - on different streams or threads without
+ * ordering between them - race, and must be serialised by the caller.
+ */
+int distri_async_groupnorm_noalloc(const distri_patch_geom *g, int64_t channels, int64_t groups,
+                                   float eps, int dtype, const void *x_fresh,
+                                   const float *stale_moments, const float *gamma,
+                                   const float *beta, void *y, float *fresh_moments, void *stream);
+
+/*
  * distri_async_groupnorm_silu - distri_async_groupnorm followed by SiLU,
  * y = z / (1 + exp(-z)) with z the normalised, affine value (GroupNorm then
  * SiLU opens each SDXL ResNet block, whose GroupNorm the wrapped module of the

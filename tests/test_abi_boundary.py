@@ -363,3 +363,26 @@ def test_cross_attention_rejects_bad_arguments(lib):
         n.value = 12345
         assert lib.distri_patch_cross_attn_workspace_size(G(*g), 10, 64, ctx, BF16, ctypes.byref(n)) == OK
         assert n.value == 0
+
+
+def test_groupnorm_noalloc_rejects_before_any_hip_call(lib):
+    """The allocation-free GroupNorm: the same argument checks, and a shape
+    whose scratch need exceeds its 2 MiB array is refused (UNSUPPORTED)."""
+    def call(geom, C=640, G=32, dtype=BF16, ptrs=None):
+        p = ptrs or [A + k * 64 * MB for k in range(6)]
+        return lib.distri_async_groupnorm_noalloc(G_(*geom), C, G, 1e-5, dtype, *p, None)
+    G_ = G
+    assert call((2, 64, 64, 8, 9)) == SHAPE
+    assert call((2, 64, 64, 8, 3), C=650) == SHAPE                # C % G != 0
+    assert call((2, 64, 64, 8, 3), dtype=9) == DTYPE
+    p = [A + k * 64 * MB for k in range(6)]
+    p[0] = None
+    assert call((2, 64, 64, 8, 3), ptrs=p) == NULL
+    p = [A + k * 64 * MB for k in range(6)]
+    p[4] = p[0] + 64                                            # y inside x_fresh
+    assert call((2, 64, 64, 8, 3), ptrs=p) == ALIAS
+    big = (4096, 8, 8, 1, 0)                                    # B * C * 8 bytes of affine alone: 32 MiB
+    assert dp.distri_async_groupnorm_workspace_size(big, 1024, 256, BF16) > 2 * MB
+    assert call(big, C=1024, G=256) == UNSUP
+    assert b"2 MiB" in lib.distri_last_error()
+    assert dp.distri_async_groupnorm_workspace_size((2, 240, 240, 8, 4), 640, 32, BF16) < 2 * MB
