@@ -125,15 +125,20 @@ class Level:
                                   t["k_stale"], t["v_stale"], out=self.out, scale=self.scale,
                                   workspace=self.attn_ws)
 
+    def refresh_maps(self, k=None, v=None, x=None, fm=None, ks=None, vs=None, xs=None, tab=None):
+        """The layer's four stale maps (K, V, conv input, moment table) as
+        (rows, row_elems, fresh, stale) for distri_refresh_stale_maps."""
+        t, wl = self.t, self.wl
+        pick = lambda a, b: b if a is None else a
+        return [(wl.h, self.tok_row, pick(k, t["k_fresh"]), pick(ks, t["k_stale"])),
+                (wl.h, self.tok_row, pick(v, t["v_fresh"]), pick(vs, t["v_stale"])),
+                (wl.h, wl.width * wl.channels, pick(x, self.y_gn), pick(xs, self.conv_stale)),
+                (1, 2 * wl.groups, pick(fm, self.fm), pick(tab, self.table))]
+
     def refresh(self):
         import displaced_patch_parallelism_distri_amd as dp
 
-        t, wl = self.t, self.wl
-        dp.distri_refresh_stale(self.geom, self.tok_row, t["k_fresh"], t["k_stale"])
-        dp.distri_refresh_stale(self.geom, self.tok_row, t["v_fresh"], t["v_stale"])
-        dp.distri_refresh_stale(self.geom, wl.width * wl.channels, self.y_gn, self.conv_stale)
-        dp.distri_refresh_stale((wl.batch, wl.n_patches, 1, wl.n_patches, wl.patch), 2 * wl.groups,
-                                self.fm, self.table)
+        dp.distri_refresh_stale_maps(self.geom, self.refresh_maps())
 
     def layer(self, ev=None):
         self.groupnorm()
@@ -183,21 +188,28 @@ def per_op(levels, iters):
         xs = [torch.randn_like(lv.t["x_fresh"], dtype=torch.float32).to(torch.bfloat16) for _ in range(nrot)]
         ys = [torch.empty_like(lv.t["x_fresh"]) for _ in range(nrot)]
         gn_med, gn_min = time_op(lambda k: lv.groupnorm(xs[k % nrot], ys[k % nrot]), iters, reps=10)
-        # refresh of the conv-input map, rotating fresh slices and stale maps
-        nrot_r = max(2, int(math.ceil(600e6 / (2 * slice_bytes + slice_bytes))))
-        stales = [torch.empty(wl.batch, wl.height, wl.width, wl.channels, dtype=torch.bfloat16,
-                              device="cuda") for _ in range(min(nrot_r, 8))]
-        nr = len(stales)
+        del xs, ys
+        # the layer's refresh, all four maps in one call (K, V, conv input,
+        # moment table), rotating through sets of fresh slices and stale maps
+        # (the contents do not matter for a bitwise copy)
         import displaced_patch_parallelism_distri_amd as dp
 
-        rf_med, rf_min = time_op(lambda k: dp.distri_refresh_stale(
-            lv.geom, wl.width * wl.channels, xs[k % nrot], stales[k % nr]), iters, reps=10)
-        del xs, ys, stales
+        t = lv.t
+        sets = []
+        for _ in range(3):
+            e = lambda a: torch.empty_like(a)
+            sets.append(lv.refresh_maps(k=e(t["k_fresh"]), v=e(t["v_fresh"]), x=e(t["x_fresh"]), fm=e(lv.fm),
+                                        ks=e(t["k_stale"]), vs=e(t["v_stale"]), xs=e(lv.conv_stale),
+                                        tab=e(lv.table)))
+        refresh_bytes = sum(m[2].numel() * m[2].element_size() for m in sets[0])
+        rf_med, rf_min = time_op(lambda k: dp.distri_refresh_stale_maps(lv.geom, sets[k % 3]), iters, reps=10)
+        del sets
         cv_med, cv_min = time_op(lambda k: lv.conv(), iters)
         at_med, at_min = time_op(lambda k: lv.attention(), iters)
         res[key] = {
             "groupnorm_ms": gn_med, "groupnorm_gbps": 2 * slice_bytes / gn_med / 1e6,
-            "refresh_ms": rf_med, "refresh_gbps": 2 * slice_bytes / rf_med / 1e6,
+            "refresh_ms": rf_med, "refresh_gbps": 2 * refresh_bytes / rf_med / 1e6,
+            "refresh_bytes_read": refresh_bytes,
             "conv_ms": cv_med, "conv_tflops": wl.conv_flops() / cv_med / 1e9,
             "attention_ms": at_med, "attention_tflops": wl.attn_flops() / at_med / 1e9,
         }
@@ -299,10 +311,13 @@ def copy_peak(iters):
     rows = 1024
     geom = (1, rows, 1, 1, 0)
     rf, _ = time_op(lambda k: dp.distri_refresh_stale(geom, nbytes // 2 // rows, src, dst), iters)
+    rm, _ = time_op(lambda k: dp.distri_refresh_stale_maps(geom, [(rows, nbytes // 2 // rows, src, dst)]),
+                    iters)
     tc, _ = time_op(lambda k: dst.copy_(src), iters)
     del src, dst
     torch.cuda.empty_cache()
     return {"refresh_kernel_gbps": round(2 * nbytes / rf / 1e6, 1),
+            "refresh_maps_kernel_gbps": round(2 * nbytes / rm / 1e6, 1),
             "torch_copy_gbps": round(2 * nbytes / tc / 1e6, 1), "bytes_copied": nbytes}
 
 
@@ -536,6 +551,7 @@ def main():
         "ms_per_layer": {"sdxl3840_l2": round(la[len(la) // 2], 4), "sdxl3840_l3": round(lb[len(lb) // 2], 4)},
         "per_op": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in ops.items()},
         "groupnorm_gbps": {k: round(v["groupnorm_gbps"], 1) for k, v in ops.items()},
+        "refresh_gbps": {k: round(v["refresh_gbps"], 1) for k, v in ops.items()},
         "hbm_copy_peak": copy,
         "projections_and_block": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in blocks.items()},
         "roofline": {"kernel": "attention at level a (attn_bf16_kernel + attn_combine_kernel)",

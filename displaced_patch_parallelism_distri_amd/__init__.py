@@ -24,14 +24,15 @@ __all__ = [
     "distri_patch_block_sync", "distri_patch_block_workspace_size",
     "distri_patch_block_sync_workspace_size", "BlockWeights", "BlockState",
     "distri_patch_cross_attn", "distri_patch_cross_attn_workspace_size", "naive_geom",
-    "distri_async_groupnorm_noalloc",
-    "DISTRI_F32", "DISTRI_BF16",
+    "distri_async_groupnorm_noalloc", "distri_refresh_stale_maps", "RefreshMap",
+    "DISTRI_F32", "DISTRI_BF16", "DISTRI_REFRESH_MAX_MAPS",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libdistri_patch.so")
 
 DISTRI_F32, DISTRI_BF16 = 0, 1
+DISTRI_REFRESH_MAX_MAPS = 8
 STATUS = {0: "OK", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_DTYPE", 4: "ERR_ALIGN",
           5: "ERR_UNSUPPORTED", 6: "ERR_WORKSPACE", 7: "ERR_HIP", 8: "ERR_ALIAS"}
 SYMBOLS = ("distri_abi_version", "distri_status_str", "distri_last_error",
@@ -42,7 +43,7 @@ SYMBOLS = ("distri_abi_version", "distri_status_str", "distri_last_error",
            "distri_patch_block_workspace_size", "distri_patch_block",
            "distri_patch_block_sync_workspace_size", "distri_patch_block_sync",
            "distri_patch_cross_attn_workspace_size", "distri_patch_cross_attn",
-           "distri_async_groupnorm_noalloc")
+           "distri_async_groupnorm_noalloc", "distri_refresh_stale_maps")
 
 
 class DistriError(RuntimeError):
@@ -62,6 +63,12 @@ class BlockWeights(ctypes.Structure):
                 ("eps", ctypes.c_float), ("scale", ctypes.c_float)] + [
         (name, ctypes.c_void_p) for name in ("gn1_gamma", "gn1_beta", "conv_w", "conv_b", "gn2_gamma",
                                              "gn2_beta", "w_qkv", "b_qkv", "w_o", "b_o")]
+
+
+class RefreshMap(ctypes.Structure):
+    """distri_refresh_map: one stale map of distri_refresh_stale_maps."""
+    _fields_ = [("rows", ctypes.c_int64), ("row_elems", ctypes.c_int64), ("dtype", ctypes.c_int),
+                ("fresh", ctypes.c_void_p), ("stale", ctypes.c_void_p)]
 
 
 class BlockState(ctypes.Structure):
@@ -93,6 +100,7 @@ def load():
     lib.distri_async_groupnorm_workspace_size.argtypes = [G, I64, I64, I, ctypes.POINTER(SZ)]
     lib.distri_async_groupnorm.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 7 + [SZ, P]
     lib.distri_refresh_stale.argtypes = [G, I64, I, P, P, P]
+    lib.distri_refresh_stale_maps.argtypes = [G, I, ctypes.POINTER(RefreshMap), P]
     lib.distri_patch_qkv_proj.argtypes = [G, I64, I] + [P] * 9
     lib.distri_patch_out_proj.argtypes = [G, I64, I] + [P] * 5
     lib.distri_async_groupnorm_silu.argtypes = [G, I64, I64, ctypes.c_float, I] + [P] * 7 + [SZ, P]
@@ -348,6 +356,24 @@ def distri_refresh_stale(g, row_elems, fresh, stale, stream=None):
         _ptr(stale, "stale", fresh.dtype, g.batch * g.height * row_elems), _stream(stream))
     _check(st, "distri_refresh_stale")
     return stale
+
+
+def distri_refresh_stale_maps(g, maps, stream=None):
+    """All of a layer's stale maps in one launch.  ``maps`` is a sequence of
+    (rows, row_elems, fresh, stale): per image, fresh [B, rows, row_elems]
+    goes to rows [i*rows, (i+1)*rows) of stale [B, n*rows, row_elems]
+    (rows = H/n for feature and K/V maps, 1 for a GroupNorm moment table).
+    Returns the stale tensors."""
+    g = _as_geom(g)
+    arr = (RefreshMap * max(len(maps), 1))()
+    for k, (rows, row_elems, fresh, stale) in enumerate(maps):
+        code = _dtype_code(fresh)
+        arr[k] = RefreshMap(rows, row_elems, code,
+                            _ptr(fresh, "fresh", fresh.dtype, g.batch * rows * row_elems),
+                            _ptr(stale, "stale", fresh.dtype, g.batch * g.n_patches * rows * row_elems))
+    st = load().distri_refresh_stale_maps(ctypes.byref(g), len(maps), arr, _stream(stream))
+    _check(st, "distri_refresh_stale_maps")
+    return [m[3] for m in maps]
 
 
 def distri_patch_qkv_proj(g, x, w_qkv, bias=None, q=None, k_fresh=None, v_fresh=None, k_stale=None,

@@ -332,6 +332,45 @@ int distri_refresh_stale(const distri_patch_geom* g, int64_t row_elems, int dtyp
                                          static_cast<hipStream_t>(stream)));
 }
 
+int distri_refresh_stale_maps(const distri_patch_geom* g, int count, const distri_refresh_map* maps,
+                              void* stream) {
+    int st = check_geom(g);
+    if (st) return st;
+    DP_CHECK(count >= 0, DISTRI_ERR_SHAPE, "count must be >= 0");
+    DP_CHECK(count <= DISTRI_REFRESH_MAX_MAPS, DISTRI_ERR_UNSUPPORTED,
+             "more than DISTRI_REFRESH_MAX_MAPS maps");
+    DP_CHECK(count == 0 || maps != nullptr, DISTRI_ERR_NULL, "maps is NULL");
+    static_assert(DISTRI_REFRESH_MAX_MAPS == dp::kRefreshMaxMaps, "map limit");
+    const dp::Geom gg = to_geom(g);
+    dp::RefreshMap rm[DISTRI_REFRESH_MAX_MAPS];
+    Range fr[DISTRI_REFRESH_MAX_MAPS], sr[DISTRI_REFRESH_MAX_MAPS];
+    for (int k = 0; k < count; ++k) {
+        const distri_refresh_map& m = maps[k];
+        st = check_dtype(m.dtype);
+        if (st) return st;
+        DP_CHECK(m.rows >= 0 && m.row_elems >= 0, DISTRI_ERR_SHAPE,
+                 "map rows and row_elems must be >= 0");
+        DP_CHECK(m.rows <= (int64_t(1) << 32) && m.row_elems <= (int64_t(1) << 32),
+                 DISTRI_ERR_UNSUPPORTED, "map rows or row_elems above 2^32");
+        const size_t eb = size_t(elem_bytes_of(m.dtype));
+        const size_t fbytes = size_t(gg.B * m.rows * m.row_elems) * eb;
+        DP_CHECK(fbytes == 0 || (m.fresh && m.stale), DISTRI_ERR_NULL, "a map pointer is NULL");
+        DP_CHECK((reinterpret_cast<uintptr_t>(m.fresh) % eb) == 0 &&
+                     (reinterpret_cast<uintptr_t>(m.stale) % eb) == 0,
+                 DISTRI_ERR_ALIGN, "map pointers must be aligned to the element size");
+        fr[k] = {m.fresh, fbytes};
+        sr[k] = {m.stale, fbytes ? size_t(gg.B * gg.n * m.rows * m.row_elems) * eb : 0};
+        rm[k] = {m.rows, m.row_elems, int(eb), m.fresh, m.stale};
+    }
+    for (int k = 0; k < count; ++k)
+        for (int j = 0; j < count; ++j) {
+            DP_CHECK(!overlaps(sr[k], fr[j]), DISTRI_ERR_ALIAS, "a stale map overlaps a fresh map");
+            DP_CHECK(j == k || !overlaps(sr[k], sr[j]), DISTRI_ERR_ALIAS,
+                     "two stale maps overlap");
+        }
+    return hip_status(dp::launch_refresh_maps(gg, count, rm, static_cast<hipStream_t>(stream)));
+}
+
 
 int distri_patch_qkv_proj(const distri_patch_geom* g, int64_t channels, int dtype, const void* x,
                           const void* w_qkv, const float* bias, void* q, void* k_fresh,

@@ -140,6 +140,16 @@ int device_cus();
 
 hipError_t launch_refresh(const Geom& g, int64_t row_elems, int elem_bytes, const void* fresh,
                           void* stale, hipStream_t s);
+// Several maps of one patch at once: map k's fresh [B, rows, row_elems]
+// goes to rows [i*rows, (i+1)*rows) of its stale [B, n*rows, row_elems].
+constexpr int kRefreshMaxMaps = 8;
+struct RefreshMap {
+    int64_t rows, row_elems;
+    int elem_bytes;
+    const void* fresh;
+    void* stale;
+};
+hipError_t launch_refresh_maps(const Geom& g, int count, const RefreshMap* maps, hipStream_t s);
 
 size_t groupnorm_workspace_bytes(const Geom& g, int64_t C, int64_t G, int elem_bytes);
 // The GroupNorm scratch array of the allocation-free entry point: its size,

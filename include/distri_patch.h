@@ -268,6 +268,38 @@ int distri_refresh_stale(const distri_patch_geom *g, int64_t row_elems, int dtyp
                          const void *fresh, void *stale, void *stream);
 
 /*
+ * distri_refresh_stale_maps - the same refresh for all of a layer's stale
+ * maps in one launch (the K and V maps of its attention, the input of its
+ * conv, its GroupNorm moment table: every activation the next step reuses,
+ * README mirror, section 概述, figure (c)).  Map m of count:
+ *   stale_m[b, i*rows_m + r, :] = fresh_m[b, r, :]   for r in [0, rows_m)
+ * with fresh_m [B, rows_m, row_elems_m] and stale_m [B, n*rows_m,
+ * row_elems_m] of dtype_m; B, n and i come from g (H and W only have to
+ * form a valid geometry).  rows_m is H/n for feature maps and K/V maps
+ * (row_elems W*C, resp. W*heads*head_dim) and 1 for a moment table
+ * (row_elems 2*G, DISTRI_F32).  Other rows are left unchanged; bitwise copy.
+ *
+ *   count   0..DISTRI_REFRESH_MAX_MAPS (DISTRI_ERR_UNSUPPORTED above)
+ *   maps    host array of count descriptors (read during the call only)
+ * A map with no elements is skipped.  Pointers must be aligned to their
+ * element size (DISTRI_ERR_ALIGN); a stale map may not overlap any fresh
+ * map or another stale map (DISTRI_ERR_ALIAS).  Maps whose rows are whole
+ * 16-byte vectors at 16-byte aligned addresses (all SDXL maps) are copied
+ * by one kernel launch; any other map gets a launch of its own on the same
+ * stream.  Every check runs before anything is enqueued.
+ */
+#define DISTRI_REFRESH_MAX_MAPS 8
+typedef struct distri_refresh_map {
+    int64_t rows;       /* rows of the fresh slice per image */
+    int64_t row_elems;  /* elements per row */
+    int dtype;          /* DISTRI_BF16 or DISTRI_F32 */
+    const void *fresh;  /* device, [B, rows, row_elems] */
+    void *stale;        /* device, [B, n * rows, row_elems] */
+} distri_refresh_map;
+int distri_refresh_stale_maps(const distri_patch_geom *g, int count, const distri_refresh_map *maps,
+                              void *stream);
+
+/*
  * distri_patch_qkv_proj - Q/K/V projection of patch i's hidden states (the
  * projections that the wrapped self-attention holds: source walkthrough,
  * section "Patch Parallelism的实现原理", item 2), with the refresh of the

@@ -175,6 +175,37 @@ def test_refresh_rejects_bad_arguments(lib):
     assert lib.distri_refresh_stale(G(*g), 0, BF16, None, None, None) == OK
 
 
+def maps_of(*entries):
+    arr = (dp.RefreshMap * max(len(entries), 1))()
+    for k, e in enumerate(entries):
+        arr[k] = dp.RefreshMap(*e)
+    return arr
+
+
+def test_refresh_maps_rejects_bad_arguments(lib):
+    g = (2, 240, 240, 8, 4)
+    h, W, C = 30, 240, 640
+    kv = (h, W * C, BF16, A, A + 512 * MB)            # a [2, 240, 240, 640] map, patch rows h
+    tab = (1, 64, F32, A + 1024 * MB, A + 1025 * MB)  # a [2, 8, 32, 2] moment table
+    call = lambda *e, count=None: lib.distri_refresh_stale_maps(
+        G(*g), len(e) if count is None else count, maps_of(*e), None)
+    assert lib.distri_refresh_stale_maps(G(*g), 0, None, None) == OK
+    assert lib.distri_refresh_stale_maps(G(*g), 2, None, None) == NULL
+    assert lib.distri_refresh_stale_maps(None, 1, maps_of(kv), None) == NULL
+    assert call(kv, count=-1) == SHAPE
+    assert call(*([kv] * 9)) == UNSUP                 # more than DISTRI_REFRESH_MAX_MAPS
+    assert call((h, W * C, 7, A, A + 512 * MB)) == DTYPE
+    assert call((-1, W * C, BF16, A, A + 512 * MB)) == SHAPE
+    assert call((h, W * C, BF16, None, A + 512 * MB)) == NULL
+    assert call((h, W * C, BF16, A + 1, A + 512 * MB)) == ALIGN
+    assert call((1, 64, F32, A + 2, A + 512 * MB)) == ALIGN
+    assert call(kv, (h, W * C, BF16, A + 256 * MB, A + 512 * MB + 64)) == ALIAS   # stale maps overlap
+    assert call(kv, (h, W * C, BF16, A + 512 * MB + 64, A + 2048 * MB)) == ALIAS  # a fresh in a stale
+    assert lib.distri_refresh_stale_maps(G(2, 240, 240, 8, 8), 1, maps_of(kv), None) == SHAPE
+    assert call((0, W * C, BF16, None, None), (h, 0, BF16, None, None)) == OK  # empty maps: nothing to do
+    assert lib.distri_refresh_stale_maps(G(0, 240, 240, 8, 4), 2, maps_of(kv, tab), None) == OK
+
+
 def test_last_error_names_the_argument(lib):
     attn(lib, (2, 64, 64, 8, 0), hd=32)
     assert b"head_dim" in lib.distri_last_error()

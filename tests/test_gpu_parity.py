@@ -134,6 +134,60 @@ def test_refresh_bitwise(wl, patch):
     assert torch.equal(tab.cpu(), ref)
 
 
+MAPS_CASES = [(W["tiny"], 1), (W["sdxl3840_l2"], 0), (W["sdxl3840_l3"], 7), (RAGGED_BF16, 3),
+              (W["sdxl3840_l2"], 4)]
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("wl,patch", MAPS_CASES, ids=_ids(MAPS_CASES))
+def test_refresh_maps_bitwise(wl, patch):
+    """All of a layer's maps in one call (K, V, the conv input, the moment
+    table, and a map of 6-byte rows that takes a launch of its own): patch
+    rows replaced bit for bit, every other row untouched."""
+    wl = wl.with_patch(patch)
+    d = cpu_inputs(wl)
+    g = gpu_copy(d)
+    B, H, Wd, h, n = wl.batch, wl.height, wl.width, wl.h, wl.n_patches
+    tok_row = Wd * wl.heads * wl.head_dim
+    odd_f = torch.arange(B * h * 3, dtype=torch.float32).to(torch.bfloat16).cuda()
+    odd_s = torch.full((B * H * 3,), -1.0, dtype=torch.bfloat16).cuda()
+    fresh_m = torch.randn(B, wl.groups, 2).cuda()
+    maps = [(h, tok_row, g["k_fresh"], g["k_stale"].clone()), (h, tok_row, g["v_fresh"], g["v_stale"].clone()),
+            (h, Wd * wl.channels, g["x_fresh"], g["x_stale"].clone()), (1, 2 * wl.groups, fresh_m, g["table"].clone()),
+            (h, 3, odd_f, odd_s)]
+    before = [m[3].cpu() for m in maps]
+    dp.distri_refresh_stale_maps(wl.geom, maps)
+    torch.cuda.synchronize()
+    for (rows, row, fresh, stale), old in zip(maps, before):
+        ref = old.clone().view(B, n * rows, row)
+        ref[:, patch * rows:(patch + 1) * rows] = fresh.cpu().view(B, rows, row)
+        assert torch.equal(_bits(stale.cpu().view(B, n * rows, row)), _bits(ref)), (rows, row)
+
+
+def test_refresh_maps_matches_single_map_calls():
+    """The one-launch form and one distri_refresh_stale per map leave the
+    same bytes (three images; per-image ranges whose sizes are off any
+    64 KiB boundary, so chunks end inside a range)."""
+    geom = (3, 40, 24, 5, 2)
+    B, H, Wd, n, i = geom
+    h = H // n
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    maps_a, maps_b = [], []
+    for row in (Wd * 8, Wd * 1000, 16):
+        fresh = torch.randn(B, h, row, generator=gen, device="cuda").to(torch.bfloat16)
+        stale = torch.randn(B, H, row, generator=gen, device="cuda").to(torch.bfloat16)
+        maps_a.append((h, row, fresh, stale.clone()))
+        dp.distri_refresh_stale(geom, row, fresh, stale)
+        maps_b.append(stale)
+    dp.distri_refresh_stale_maps(geom, maps_a)
+    torch.cuda.synchronize()
+    for (_, _, _, got), want in zip(maps_a, maps_b):
+        assert torch.equal(_bits(got), _bits(want))
+
+
 def test_refresh_odd_rows_and_alignment():
     """Rows whose byte size is not a multiple of 16 (scalar path)."""
     geom = (3, 6, 1, 3, 1)
@@ -243,13 +297,18 @@ def test_extreme_scores_stay_finite():
 # GroupNorm launch shapes away from the SDXL ones: groups that split a
 # 16-byte channel vector (C/G = 4), one group, block widths that are not a
 # power of two (C = 40 -> 5 vectors per pixel), fp32, and more chunks than
-# one block row covers.
+# one block row covers.  The last two take the three-launch form: more than
+# 256 images (the single-launch form holds at most 256 blocks, one image or
+# more per block), and a slice of more than 32 pixels per thread at 256
+# blocks.
 GN_SHAPES = [si.Workload("gn_c40_g5", 2, 40, 12, 10, 3, 1, groups=5, seed=3001, patch=1),
              si.Workload("gn_c1024_g256", 1, 1024, 8, 6, 2, 1, groups=256, seed=3002, patch=1),
              si.Workload("gn_c64_g1", 3, 64, 16, 9, 4, 1, groups=1, seed=3003, patch=3),
              si.Workload("gn_f32_c12_g3", 2, 12, 10, 11, 5, 1, groups=3, dtype="f32", sigma=0.05,
                          seed=3004, patch=2),
-             si.Workload("gn_c2048_g32", 3, 2048, 32, 24, 4, 1, groups=32, seed=3005, patch=0)]
+             si.Workload("gn_c2048_g32", 3, 2048, 32, 24, 4, 1, groups=32, seed=3005, patch=0),
+             si.Workload("gn_b257_three_launch", 257, 32, 8, 8, 2, 1, groups=8, seed=3006, patch=1),
+             si.Workload("gn_big_slice_three_launch", 1, 1024, 184, 184, 1, 1, groups=32, seed=3007)]
 
 
 @pytest.mark.parametrize("wl", GN_SHAPES, ids=[w.name for w in GN_SHAPES])
@@ -285,6 +344,30 @@ def test_groupnorm_reused_workspace_is_exact():
                                           workspace=shared)
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int16), ref_y.view(torch.int16)), f"call {k}"
+        assert torch.equal(fm, ref_fm), f"call {k}"
+
+
+def test_groupnorm_workspace_shared_across_shapes():
+    """One workspace serves, in turn, GroupNorms of different shapes (so of
+    different block counts, with flags of one shape's calls left where the
+    other shape's blocks look) and the moments-only, normalise and SiLU
+    forms; every call must give the bits of a call on a zeroed workspace."""
+    wls = [W["sdxl1024_l2"].with_patch(3), W["sdxl1024_l3"].with_patch(0), W["tiny"].with_patch(1)]
+    ins = [(wl, gpu_copy(cpu_inputs(wl))) for wl in wls]
+    nb = max(dp.distri_async_groupnorm_workspace_size(wl.geom, wl.channels, wl.groups,
+                                                      dp.DISTRI_BF16 if wl.dtype == "bf16" else dp.DISTRI_F32)
+             for wl in wls)
+    shared = torch.randint(0, 255, (nb,), dtype=torch.uint8, device="cuda")
+    for k in range(7):
+        wl, g = ins[k % len(ins)]
+        fn = dp.distri_async_groupnorm_silu if k % 2 else dp.distri_async_groupnorm
+        ref_y, ref_fm = fn(wl.geom, wl.groups, g["x_fresh"], g["table"], g["gamma"], g["beta"],
+                           eps=wl.eps, workspace=torch.zeros(nb, dtype=torch.uint8, device="cuda"))
+        y, fm = fn(wl.geom, wl.groups, g["x_fresh"], g["table"], g["gamma"], g["beta"], eps=wl.eps,
+                   workspace=shared)
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16 if wl.dtype == "bf16" else torch.int32),
+                           ref_y.view(torch.int16 if wl.dtype == "bf16" else torch.int32)), f"call {k}"
         assert torch.equal(fm, ref_fm), f"call {k}"
 
 
