@@ -358,7 +358,7 @@ def cpu_baseline(budget_s):
             "seconds": round(ta + tc, 2)}
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sdxl3840_l2_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sdxl3840_traffic_counters.md")
 ATTN_SRC = os.path.join(ROOT, "displaced_patch_parallelism_distri_amd", "csrc", "attention.hip")
 
 

@@ -167,26 +167,30 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
 #pragma unroll
         for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Both k32 halves' operand fragments are read first, so the second
+    // half's LDS reads are in flight while the first half's MFMAs run.
     auto compute = [&](int cur) {
+        bf16x8 af[BK / 32][MT], bf[BK / 32][NT];
 #pragma unroll
         for (int kk = 0; kk < BK / 32; ++kk) {
-            bf16x8 af[MT], bf[NT];
 #pragma unroll
             for (int i = 0; i < MT; ++i) {
                 const int row = wm * WM + i * 16 + l16;
-                af[i] = *reinterpret_cast<const bf16x8*>(&a_lds[cur][row * BK + swz(row, kk * 4 + lq) * 8]);
+                af[kk][i] = *reinterpret_cast<const bf16x8*>(&a_lds[cur][row * BK + swz(row, kk * 4 + lq) * 8]);
             }
 #pragma unroll
             for (int j = 0; j < NT; ++j) {
                 const int row = wn * WN + j * 16 + l16;
-                bf[j] = *reinterpret_cast<const bf16x8*>(&b_lds[cur][row * BK + swz(row, kk * 4 + lq) * 8]);
+                bf[kk][j] = *reinterpret_cast<const bf16x8*>(&b_lds[cur][row * BK + swz(row, kk * 4 + lq) * 8]);
             }
+        }
+#pragma unroll
+        for (int kk = 0; kk < BK / 32; ++kk)
 #pragma unroll
             for (int i = 0; i < MT; ++i)
 #pragma unroll
                 for (int j = 0; j < NT; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kk][i], bf[kk][j], acc[i][j], 0, 0, 0);
     };
     // step s: its loads are done, then the barrier (every wave's share is
     // in LDS and every wave has left step s - 1, whose buffer the loads of
