@@ -70,8 +70,13 @@ template <int BM>
 __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
     constexpr int WM = BM / 2, MT = WM / 16;
     constexpr int A_CHUNKS = BM * 8 / 256;
-    __shared__ __attribute__((aligned(16))) uint16_t a_lds[2][BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t b_lds[2][BN * BK];
+    // the two tile buffers, and after the K loop the bf16 output tile
+    // [BM][OUT_PITCH] staged for 16-byte stores
+    constexpr int OUT_PITCH = BN + 8;  // 336-byte rows: 4 rows apart land on other banks
+    static_assert(BM * OUT_PITCH <= 2 * (BM + BN) * BK, "output tile fits the tile buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (BM + BN) * BK];
+    uint16_t (*a_lds)[BM * BK] = reinterpret_cast<uint16_t (*)[BM * BK]>(smem);
+    uint16_t (*b_lds)[BN * BK] = reinterpret_cast<uint16_t (*)[BN * BK]>(smem + 2 * BM * BK);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -206,7 +211,38 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
     }
 
     // epilogue: acc[i][j][e] is pixel m0 + wm*WM + i*16 + 4*lq + e,
-    // cout n0 + wn*80 + j*16 + l16
+    // cout n0 + wn*80 + j*16 + l16.  With Cout a multiple of 8 the tile is
+    // staged in LDS as bf16 and written out in 16-byte pieces of a pixel's
+    // channel run (whole 64-byte segments instead of 2-byte scatters);
+    // otherwise each element is stored on its own.
+    const bool vec_out = (a.cout % 8) == 0 && (reinterpret_cast<uintptr_t>(a.y) % 16) == 0;
+    if (vec_out) {
+        __syncthreads();  // every wave is past its last tile read
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            const int c = wn * WN + j * 16 + l16;
+            const int n = n0 + c;
+            const float bias = (a.bias && n < a.cout) ? a.bias[n] : 0.f;
+#pragma unroll
+            for (int i = 0; i < MT; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int r = wm * WM + i * 16 + 4 * lq + e;
+                    smem[r * OUT_PITCH + c] = f32_to_bf16(acc[i][j][e] + bias);
+                }
+        }
+        __syncthreads();
+        constexpr int CHUNKS = BN / 8;  // 16-byte pieces per tile row
+        const int ncol = a.cout - n0 < BN ? (a.cout - n0) / 8 : CHUNKS;
+        for (int t = tid; t < BM * CHUNKS; t += 256) {
+            const int r = t / CHUNKS, ch = t - r * CHUNKS;
+            const int m = m0 + r;
+            if (m < a.M && ch < ncol)
+                *reinterpret_cast<u32x4*>(a.y + size_t(m) * a.cout + n0 + ch * 8) =
+                    *reinterpret_cast<const u32x4*>(&smem[r * OUT_PITCH + ch * 8]);
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
         const int n = n0 + wn * WN + j * 16 + l16;

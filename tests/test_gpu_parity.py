@@ -188,6 +188,24 @@ def test_refresh_maps_matches_single_map_calls():
         assert torch.equal(_bits(got), _bits(want))
 
 
+@pytest.mark.parametrize("cout", [200, 90, 8, 160], ids=["cout200", "cout90", "cout8", "cout160"])
+def test_conv_output_channel_counts(cout):
+    """Cout other than Cin: a partial 160-channel tile (200), a count that is
+    not a multiple of 8 (90: element stores instead of the staged 16-byte
+    ones), a tile of 8 channels, and exactly one tile."""
+    geom = (2, 12, 11, 3, 1)
+    B, H, Wd, n, i = geom
+    h, cin = H // n, 64
+    gen = torch.Generator().manual_seed(4100 + cout)
+    xf = torch.randn(B, h, Wd, cin, generator=gen).to(torch.bfloat16)
+    xs = torch.randn(B, H, Wd, cin, generator=gen).to(torch.bfloat16)
+    w = (torch.randn(cout, 3, 3, cin, generator=gen) / 24.0).to(torch.bfloat16)
+    bias = 0.1 * torch.randn(cout, generator=gen)
+    y = dp.distri_patch_conv3x3_halo(geom, xf.cuda(), xs.cuda(), w.cuda(), bias.cuda())
+    ref = oracle.patch_conv3x3_halo(geom, cin, cout, xf, xs, w, bias)
+    assert_close(to_np(y), ref, "bf16", f"conv cout {cout}")
+
+
 def test_refresh_odd_rows_and_alignment():
     """Rows whose byte size is not a multiple of 16 (scalar path)."""
     geom = (3, 6, 1, 3, 1)
