@@ -13,8 +13,9 @@
 //    resident at once and keeps its chunk of x in registers across a
 //    grid-wide hand-off, so x is read from HBM once and y written once; the
 //    kernel's comment below has the details;
-//  * three launches, for slices too large to hold in the registers of 256
-//    blocks (more than 32 pixels per thread) or more than 256 images:
+//  * three launches, for slices too large to hold in the registers of
+//    kFusedMaxBlocks blocks (more than 16 pixels per thread) or more images
+//    than that:
 //   1. gn_moments   - coalesced pass over x [B, h*W, C] (NHWC).  A block is a
 //                     (rows x vectors-per-pixel) grid of threads: thread
 //                     (row, col) owns one 16-byte channel vector of KV pixels
@@ -358,12 +359,12 @@ __global__ __launch_bounds__(kMaxThreads) void gn_normalize(GnArgs a) {
 // slots are read with agent-scope atomic loads.  The wait is bounded: a
 // block that times out (a launch that could not be made resident, which the
 // occupancy check rules out) turns its output to NaN instead of hanging.
-// Measured on MI355X at the SDXL 3840 shapes, one launch takes 16.7 us
-// (level a, 36.9 MB moved) and 13.5 us (level b, 18.4 MB), against 20.4 and
-// 20.2 us for the three-launch form: the x loads complete about 6 us after
+// Measured on MI355X at the SDXL 3840 shapes, one launch takes about 16
+// us (level a, 36.9 MB moved) and 12-13.5 us (level b, 18.4 MB), against
+// 20.4 and 20.2 us for the three-launch form: the x loads complete about 6 us after
 // the first block starts, and the hand-off (slot stores, flags, slot loads)
 // adds a chain of dependent memory round trips of about 1-2.5 us each.
-constexpr int kFusedMaxBlocks = 256;
+constexpr int kFusedMaxBlocks = 192;  // 128-256 measured: 192 is 2-4% ahead at the SDXL shapes
 constexpr int kFusedThreads = 512;
 constexpr int kFusedMaxKV = 16;
 constexpr int kSpinLimit = 1 << 20;  // polls of ~100 cycles: ~50 ms

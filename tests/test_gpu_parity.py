@@ -316,7 +316,7 @@ def test_extreme_scores_stay_finite():
 # 16-byte channel vector (C/G = 4), one group, block widths that are not a
 # power of two (C = 40 -> 5 vectors per pixel), fp32, and more chunks than
 # one block row covers.  The last two take the three-launch form: more than
-# 256 images (the single-launch form holds at most 256 blocks, one image or
+# 256 images (the single-launch form holds at most 192 blocks, one image or
 # more per block), and a slice of more than 32 pixels per thread at 256
 # blocks.
 GN_SHAPES = [si.Workload("gn_c40_g5", 2, 40, 12, 10, 3, 1, groups=5, seed=3001, patch=1),
