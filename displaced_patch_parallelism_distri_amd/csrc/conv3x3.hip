@@ -31,8 +31,12 @@
 //    ds_read_b128 operand reads free of bank conflicts without padding
 //    (2 x 72 KB fit per CU); a load's LDS slot is fixed by its lane, so each
 //    thread reads the logical chunk that the swizzle puts in its slot.
-//  * Blocks are remapped so that each XCD works through the tiles of one or
-//    two cout slices: their weights stay in that XCD's L2.
+//  * Blocks are remapped so that each XCD takes every cout slice of one
+//    contiguous range of pixel tiles: a pixel row is fetched into the XCD's
+//    L2 once for all slices and stays there for the neighbouring taps, and
+//    a step's weights (all slices, 64 channels) are shared by the XCD's
+//    blocks.  (Measured on MI355X against slice-major order: same time at
+//    Cout 640 / BM 128, 4% faster at Cout 1280 / BM 64.)
 // fp32 kernel: one thread per output element, direct sum; parity-grade.
 #include "dp_common.h"
 
@@ -83,13 +87,14 @@ __global__ __launch_bounds__(256, 2) void conv_bf16_kernel(ConvArgs a) {
     const int l16 = lane & 15, lq = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // XCD-aware tile order: logical tiles run cout-slice-major; the blocks
-    // of one XCD (physical id % 8) take a contiguous logical range
+    // XCD-aware tile order: logical tiles run pixel-tile-major with the cout
+    // slices inner; the blocks of one XCD (physical id % 8) take a
+    // contiguous logical range
     const int ntot = a.mtiles * a.ntiles;
     const int n8 = ntot - ntot % 8;
     const int pw = blockIdx.x;
     const int logical = pw < n8 ? (pw % 8) * (n8 / 8) + pw / 8 : pw;
-    const int nt = logical / a.mtiles, mt = logical % a.mtiles;
+    const int mt = logical / a.ntiles, nt = logical % a.ntiles;
     const int m0 = mt * BM, n0 = nt * BN;
 
     // ---- A loader: chunk c = tid + 256 j -> row c / 8, 16-byte chunk c % 8

@@ -70,8 +70,8 @@ __global__ __launch_bounds__(256, 2) void proj_bf16_kernel(ProjArgs a) {
     const int l16 = lane & 15, lq = lane >> 4;
     const int wm = wave >> 1, wn = wave & 1;
 
-    // XCD-aware tile order (as in the conv kernel): each XCD walks the
-    // tiles of one or two output-column slices, whose weights stay in its L2
+    // XCD-aware tile order: each XCD walks the tiles of one or two
+    // output-column slices, whose weights stay in its L2
     const int ntot = a.mtiles * a.ntiles;
     const int n8 = ntot - ntot % 8;
     const int pw = blockIdx.x;
