@@ -60,8 +60,9 @@
 //    details): a wave's tile work splits into an MFMA phase and a VALU
 //    (softmax) phase, and the two waves that share a SIMD run them in
 //    opposite order, so one issues MFMAs while the other runs its softmax.
-//    gfx950 overlaps MFMA work with exp / fma / cvt work of another wave,
-//    but not with the dot instructions, so the softmax sums P without them.
+//    gfx950 co-issues exp / fma / cvt work of one wave beside another
+//    wave's MFMAs, but hardly the dot instructions, so the softmax sums P
+//    without them.
 // fp32 kernel: one thread per query, K/V tiles in LDS, fp32 online softmax
 // with expf; used for fp32 inputs (parity-grade, small workloads).
 #include "dp_common.h"
@@ -441,11 +442,14 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
     // A CU holds two waves per SIMD, waves w and w+4.  Waves 4-7 run each tile
     // as alpha(k) then beta(k+1); waves 0-3 as beta(k) then alpha(k), half a
     // tile behind.  So while one wave of a SIMD issues its MFMA phase the
-    // other issues its VALU phase: gfx950 overlaps MFMA and VALU work of
-    // different waves almost fully, but barely within one wave.  The VALU
-    // phase is the longer one, and the issue arbiter favours the older waves
-    // (0-3) when both have VALU work, so those run the softmax first.  The
-    // tile loads and the V conversion ride in the VALU phase of both groups.
+    // other issues its VALU phase.  (gfx950 overlaps an MFMA-only wave with
+    // a VALU-only wave on one SIMD well; with short alternating phases, as
+    // here, a register-only probe overlapped them far less.  Measured with
+    // the tile loads in, this order still beats both groups running the
+    // same order.)  The VALU phase is the longer one, and the issue arbiter
+    // favours the older waves (0-3) when both have VALU work, so those run
+    // the softmax first.  The tile loads and the V conversion ride in the
+    // VALU phase of both groups.
     // One barrier per tile, before both groups' work on tile k: after it tile
     // k+1 is in LDS (S over it in alpha(k)), V of tile k is f16 and visible
     // (converted during tile k-1), and every wave is past its last read of
