@@ -253,7 +253,33 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
     const uint16_t* vst = a.vs + (b * a.L * a.heads + hd) * D;
     const uint16_t* kfr = a.kf + (b * a.lq * a.heads + hd) * D;
     const uint16_t* vfr = a.vf + (b * a.lq * a.heads + hd) * D;
+    // Tiles whose 64 rows all lie inside the map: the thread's row pointers
+    // advance by one tile stride (a wave-uniform offset), the fresh / stale
+    // choice is one compare and two selects, the LDS slot is wave-uniform.
+    // The map's last, partial tile takes the clamped per-row path below.
+    static_assert(TROWS == 1, "one K and one V row per thread and tile");
+    const int krow0 = tid >> 3;
+    const uint64_t kst0 = reinterpret_cast<uint64_t>(kst + int64_t(krow0) * rs + (c8 ^ k_swizzle(krow0)) * 8);
+    const uint64_t vst0 = reinterpret_cast<uint64_t>(vst + int64_t(krow0) * rs + (c8 ^ v_swizzle(krow0)) * 8);
+    // fresh rows: row t sits at (t - own_lo) * rs of the fresh slice; the
+    // address is formed for every row but used only where the row is fresh
+    const uint64_t fshift = uint64_t(int64_t(a.own_lo) * rs * 2);
+    const uint64_t kfr0 = reinterpret_cast<uint64_t>(kfr + int64_t(krow0) * rs + (c8 ^ k_swizzle(krow0)) * 8) - fshift;
+    const uint64_t vfr0 = reinterpret_cast<uint64_t>(vfr + int64_t(krow0) * rs + (c8 ^ v_swizzle(krow0)) * 8) - fshift;
+    const uint32_t wslot = uint32_t(__builtin_amdgcn_readfirstlane(wave)) * 64 * 16;
+    const int full_tiles = a.L / KT;
     auto tile_load = [&](int kt, int stage) {
+        if (kt < full_tiles) {
+            // bytes from tile 0: below 2^32, as the map's bytes are (the ABI
+            // bounds L * heads * D below 2^31 elements)
+            const uint32_t d = __builtin_amdgcn_readfirstlane(uint32_t(kt) * uint32_t(KT * 2 * rs));
+            const bool fresh = unsigned(kt * KT + krow0 - a.own_lo) < unsigned(a.lq);
+            const uint16_t* kp = reinterpret_cast<const uint16_t*>((fresh ? kfr0 : kst0) + d);
+            const uint16_t* vp = reinterpret_cast<const uint16_t*>((fresh ? vfr0 : vst0) + d);
+            global_load_lds16(kp, lds_addr(&kv_lds[stage][0][0]) + wslot);
+            global_load_lds16(vp, lds_addr(&kv_lds[stage][1][0]) + wslot);
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < TROWS; ++j) {
             const int krow = (tid >> 3) + j * NWAVES * 8;
