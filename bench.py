@@ -93,11 +93,12 @@ class Level:
         self.conv_stale = d["x_stale"]          # stale conv input map (GN output of last step)
         self.y_gn = torch.empty_like(d["x_fresh"])
         self.fm = torch.empty(B, G, 2, dtype=torch.float32, device=dev)
-        self.y_conv = torch.empty(B, wl.h, wl.width, C, dtype=torch.bfloat16, device=dev)
+        code = dp.DISTRI_BF16 if wl.dtype == "bf16" else dp.DISTRI_F32
+        self.y_conv = torch.empty(B, wl.h, wl.width, C, dtype=d["x_fresh"].dtype, device=dev)
         self.out = torch.empty_like(d["q"])
-        self.gn_ws = torch.empty(dp.distri_async_groupnorm_workspace_size(self.geom, C, G, dp.DISTRI_BF16),
+        self.gn_ws = torch.empty(dp.distri_async_groupnorm_workspace_size(self.geom, C, G, code),
                                  dtype=torch.uint8, device=dev)
-        nb = dp.distri_patch_self_attn_workspace_size(self.geom, wl.heads, 64, dp.DISTRI_BF16)
+        nb = dp.distri_patch_self_attn_workspace_size(self.geom, wl.heads, 64, code)
         self.attn_ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=dev)
         self.tok_row = wl.width * wl.heads * wl.head_dim
         self.scale = wl.head_dim ** -0.5
@@ -358,6 +359,91 @@ def cpu_baseline(budget_s):
             "seconds": round(ta + tc, 2)}
 
 
+SMALL_CONFIGS = ("tiny", "sdxl1024_l2", "sdxl1024_l3")
+
+
+def _small_patch(wl):
+    return wl.n_patches // 2
+
+
+def oracle_one_core():
+    """The oracle's time per op on one host core (its OpenMP thread count set
+    to 1 for these calls, then restored) on the three small configurations,
+    interior patch.  Attention runs on the first min(Lq, 64) local query
+    rows and the conv on one output row; both are scaled to the whole patch
+    by the row count (their cost is linear in it).  GroupNorm runs whole."""
+    import numpy as np
+
+    import oracle
+    import synthetic_inputs as si
+
+    before = oracle.num_threads()
+    oracle.set_num_threads(1)
+    res = {"threads": oracle.num_threads()}
+    for name in SMALL_CONFIGS:
+        base = si.WORKLOADS[name]
+        wl = base.with_patch(_small_patch(base))
+        d = si.make_inputs(wl, device="cpu", nonzero_bias=True)
+        f = {k: np.ascontiguousarray(v.double().numpy()) for k, v in d.items()}
+        B, n, G, h = wl.batch, wl.n_patches, wl.groups, wl.h
+        table = np.zeros((B, n, G, 2))
+        for j in range(n):
+            table[:, j] = oracle.group_moments(f["x_stale"][:, j * h:(j + 1) * h], G)
+        ra = min(wl.lq, 64)
+        t0 = time.perf_counter()
+        oracle.patch_self_attn(wl.geom, wl.heads, 64, wl.head_dim ** -0.5, f["q"], f["k_fresh"], f["v_fresh"],
+                               f["k_stale"], f["v_stale"], rows=(0, ra))
+        ta = (time.perf_counter() - t0) * wl.lq / ra
+        t0 = time.perf_counter()
+        oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, f["x_fresh"], f["x_stale"], f["weight"],
+                                  f["bias"], rows=(0, 1))
+        tc = (time.perf_counter() - t0) * h
+        t0 = time.perf_counter()
+        oracle.async_groupnorm(wl.geom, wl.channels, G, wl.eps, f["x_fresh"], table, f["gamma"], f["beta"])
+        tg = time.perf_counter() - t0
+        res[name] = {"attention_ms": ta * 1e3, "conv_ms": tc * 1e3, "groupnorm_ms": tg * 1e3,
+                     "sample": f"patch {wl.patch} of {n}; attention {ra} of {wl.lq} query rows and conv "
+                               f"1 of {h} output rows, scaled by the row count; GroupNorm whole"}
+    oracle.set_num_threads(before)
+    return res
+
+
+def cpu_info():
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
+def small_config_comparison(iters):
+    """The oracle on one host core against the kernels on the GPU, per op,
+    on the three small configurations."""
+    import torch
+
+    cpu = oracle_one_core()
+    dev = torch.device("cuda:0")
+    out = {"oracle_threads": cpu.pop("threads")}
+    for name in SMALL_CONFIGS:
+        base = __import__("synthetic_inputs").WORKLOADS[name]
+        lv = Level(name, _small_patch(base), dev)
+        gpu = {"attention_ms": time_op(lambda k: lv.attention(), iters)[0],
+               "conv_ms": time_op(lambda k: lv.conv(), iters)[0],
+               "groupnorm_ms": time_op(lambda k: lv.groupnorm(), iters, reps=10)[0]}
+        row = {"dtype": lv.wl.dtype, "sample": cpu[name]["sample"]}
+        for op in ("attention", "conv", "groupnorm"):
+            c, g = cpu[name][op + "_ms"], gpu[op + "_ms"]
+            row[op] = {"oracle_1core_ms": round(c, 3), "gpu_ms": round(g, 4), "speedup": round(c / g, 1)}
+        out[name] = row
+        del lv
+    torch.cuda.empty_cache()
+    return out
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_sdxl3840_traffic_counters.md")
 ATTN_SRC = os.path.join(ROOT, "displaced_patch_parallelism_distri_amd", "csrc", "attention.hip")
 
@@ -562,6 +648,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        out["cpu_baseline"].update(cpu_info())
+        out["cpu_baseline"]["small_configs_one_core"] = small_config_comparison(args.op_iters)
     print(json.dumps(out), flush=True)
 
 

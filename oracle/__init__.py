@@ -40,6 +40,8 @@ def _load():
     if _lib is None:
         lib = ctypes.CDLL(build())
         lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
         lib.oracle_patch_self_attn.argtypes = [_I] * 7 + [ctypes.c_double] + [_D] * 5 + [_I, _I, _D]
         lib.oracle_patch_conv3x3_halo.argtypes = [_I] * 7 + [_D] * 4 + [_I, _I, _D]
         lib.oracle_group_moments.argtypes = [_I] * 5 + [_D, _D]
@@ -79,6 +81,11 @@ def _check(rc, name):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads of the calls that follow (for timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def patch_self_attn(geom, heads, head_dim, scale, q, k_fresh, v_fresh, k_stale, v_stale,

@@ -59,6 +59,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads the following calls use (timing on a given number of host cores);
+ * no effect on any result. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* Patch self-attention for local query rows [r0, r1) of patch i.
  * out holds (r1 - r0) rows: out[b, r - r0, head, :]. */
 int oracle_patch_self_attn(int64_t B, int64_t H, int64_t W, int64_t n, int64_t i,

@@ -327,3 +327,34 @@ def test_oracle_rejects_bad_geometry():
         oracle.patch_self_attn((1, 5, 1, 2, 0), 1, 1, 1.0, x, x, x, x, x)
     with pytest.raises(ValueError):
         oracle.async_groupnorm((1, 2, 1, 2, 2), 2, 1, 0.0, np.zeros((1, 1, 1, 2)), np.zeros((1, 2, 1, 2)))
+
+
+def test_thread_count_changes_no_result():
+    """Every output element is computed by one thread in a fixed order, so the
+    oracle's results are the same bits on one host thread as on all of them
+    (the benchmark times it both ways)."""
+    wl = si.WORKLOADS["tiny"].with_patch(1)
+    d = {k: v.double().numpy() for k, v in si.make_inputs(wl, device="cpu", nonzero_bias=True).items()}
+    B, n, G, h = wl.batch, wl.n_patches, wl.groups, wl.h
+    table = np.stack([oracle.group_moments(d["x_stale"][:, j * h:(j + 1) * h], G) for j in range(n)], axis=1)
+
+    def run():
+        a = oracle.patch_self_attn(wl.geom, wl.heads, 64, wl.head_dim ** -0.5, d["q"], d["k_fresh"],
+                                   d["v_fresh"], d["k_stale"], d["v_stale"])
+        c = oracle.patch_conv3x3_halo(wl.geom, wl.channels, wl.channels, d["x_fresh"], d["x_stale"],
+                                      d["weight"], d["bias"])
+        g, fm = oracle.async_groupnorm(wl.geom, wl.channels, G, wl.eps, d["x_fresh"], table, d["gamma"],
+                                       d["beta"])
+        return a, c, g, fm
+
+    before = oracle.num_threads()
+    try:
+        many = run()
+        oracle.set_num_threads(1)
+        assert oracle.num_threads() == 1
+        one = run()
+    finally:
+        oracle.set_num_threads(before)
+    assert oracle.num_threads() == before
+    for x, y in zip(many, one):
+        assert np.array_equal(x, y)
