@@ -573,8 +573,8 @@ __global__ __launch_bounds__(NWAVES * 64, BLOCKS_PER_CU) void attn_bf16_kernel(A
         __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     convert_v(0);
-    // S over the first tile; waves 0-3 also its softmax (their first phase
-    // is alpha, which needs P)
+    // S over the first tile; waves 4-7 also its softmax (their first phase
+    // in the loop is alpha, which needs P)
     if (wave_active) {
         qk2(0, s[0], s[1]);
         if (grp == 0) beta(kt0);
